@@ -1,0 +1,298 @@
+// C ABI of libstattn: argument checks, workspace layout and launch sequencing.
+// The operations are described in include/st_attn.h.
+#include "st_attn.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "st_internal.h"
+
+namespace st {
+
+RopeGeom make_geom(int T, int H, int W, const int split[3]) {
+    RopeGeom g;
+    g.T = T;
+    g.H = H;
+    g.W = W;
+    g.S = H * W;
+    g.Nv = T * H * W;
+    g.inv_S = 1.0f / (float)g.S;
+    g.inv_W = 1.0f / (float)W;
+    for (int a = 0; a < 3; ++a) g.pairs[a] = split[a] / 2;
+    g.first[0] = 0;
+    g.first[1] = g.pairs[0];
+    g.first[2] = g.pairs[0] + g.pairs[1];
+    g.off[0] = 0;
+    g.off[1] = T * g.pairs[0];
+    g.off[2] = g.off[1] + H * g.pairs[1];
+    g.identity = g.off[2] + W * g.pairs[2];
+    return g;
+}
+
+}  // namespace st
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr long long kMaxRows = 1LL << 24;
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool grid_ok(int T, int H, int W, int n_text, long long* n_out) {
+    if (T < 1 || H < 1 || W < 1 || n_text < 0) return false;
+    long long nv = (long long)T * H * W;
+    long long n = nv + n_text;
+    if (n >= kMaxRows) return false;
+    if (n_out) *n_out = n;
+    return true;
+}
+
+st_status check_split(const int* split, int d) {
+    if (!split) return ST_ERR_NULL;
+    long long sum = 0;
+    for (int a = 0; a < 3; ++a) {
+        if (split[a] < 0 || (split[a] & 1)) return ST_ERR_SPLIT;
+        sum += split[a];
+    }
+    if (sum != d) return ST_ERR_SPLIT;
+    return ST_OK;
+}
+
+size_t table_bytes_for(int T, int H, int W, const int* split) {
+    long long entries = (long long)T * (split[0] / 2) + (long long)H * (split[1] / 2) +
+                        (long long)W * (split[2] / 2) + 1;
+    return align_up((size_t)entries * sizeof(float2), kWsAlign);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bn && b0 < a0 + an;
+}
+
+size_t elem_size(st_dtype dt) { return dt == ST_BF16 ? 2 : 4; }
+
+bool theta_ok(float theta) { return isfinite(theta) && theta > 0.0f; }
+
+// Checks shared by the attention entry points (tensor pointers, shapes, dtype, split, aliasing).
+st_status check_attn(const void* q, const void* k, const void* v, const void* out, int T, int H,
+                     int W, int n_text, int heads, int d, const int* split, st_dtype dtype,
+                     long long* n_out) {
+    if (!q || !k || !v || !out) return ST_ERR_NULL;
+    if (!split) return ST_ERR_NULL;
+    long long n = 0;
+    if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
+    if (heads < 1 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
+    if ((long long)n * heads * d >= (1LL << 40)) return ST_ERR_SHAPE;
+    st_status s = check_split(split, d);
+    if (s != ST_OK) return s;
+    if (dtype == ST_BF16) {
+        if (d != 128) return ST_ERR_UNSUPPORTED;
+    } else if (dtype == ST_F32) {
+        if (d > 128) return ST_ERR_UNSUPPORTED;
+    } else {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (heads > 65535) return ST_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return ST_ERR_ALIGN;
+    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
+    if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
+        overlaps(out, bytes, v, bytes))
+        return ST_ERR_ALIAS;
+    *n_out = n;
+    return ST_OK;
+}
+
+st_status hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return ST_ERR_HIP;
+}
+
+// Launch the attention kernels for one of the two modes, given a built table.
+hipError_t run_full(const void* q, const void* k, const void* v, void* out, const st::RopeGeom& g,
+                    int n, int heads, int d, st_dtype dtype, const float2* table,
+                    hipStream_t stream) {
+    if (dtype == ST_BF16)
+        return st::launch_attn_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                    (uint16_t*)out, table, g, n, heads, n, 1, stream);
+    return st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out,
+                               table, g, heads, d, 1, n, 0, 1, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t st_rope3d_table_bytes(int T, int H, int W, const int rope_split[3]) {
+    if (!rope_split || !grid_ok(T, H, W, 0, nullptr)) return 0;
+    for (int a = 0; a < 3; ++a)
+        if (rope_split[a] < 0 || (rope_split[a] & 1)) return 0;
+    return table_bytes_for(T, H, W, rope_split);
+}
+
+st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], float theta,
+                                void* table, size_t table_bytes, hipStream_t stream) {
+    if (!rope_split || !table) return ST_ERR_NULL;
+    if (!grid_ok(T, H, W, 0, nullptr)) return ST_ERR_SHAPE;
+    for (int a = 0; a < 3; ++a)
+        if (rope_split[a] < 0 || (rope_split[a] & 1)) return ST_ERR_SPLIT;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!aligned(table, kWsAlign)) return ST_ERR_ALIGN;
+    if (table_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    hipError_t e = st::launch_rope_table(g, (double)theta, (float2*)table, stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+size_t st_attn3d_workspace_bytes(int T, int H, int W, const int rope_split[3]) {
+    return st_rope3d_table_bytes(T, H, W, rope_split);
+}
+
+st_status st_attn3d_fwd_tabled(const void* q, const void* k, const void* v, int T, int H, int W,
+                               int n_text, int heads, int d, const int rope_split[3],
+                               st_dtype dtype, const void* table, size_t table_bytes, void* out,
+                               hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!table) return ST_ERR_NULL;
+    if (!aligned(table, kWsAlign)) return ST_ERR_ALIGN;
+    if (table_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    hipError_t e = run_full(q, k, v, out, g, (int)n, heads, d, dtype, (const float2*)table, stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                        int n_text, int heads, int d, const int rope_split[3], float theta,
+                        st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
+                        hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!workspace) return ST_ERR_NULL;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    if (ws_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
+    if (overlaps(workspace, ws_bytes, out, bytes) || overlaps(workspace, ws_bytes, q, bytes) ||
+        overlaps(workspace, ws_bytes, k, bytes) || overlaps(workspace, ws_bytes, v, bytes))
+        return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    float2* table = (float2*)workspace;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = run_full(q, k, v, out, g, (int)n, heads, d, dtype, table, stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
+                                          const int rope_split[3], st_dtype dtype) {
+    if (!rope_split || heads < 1 || d < 2 || (d & 1)) return 0;
+    if (dtype != ST_BF16 && dtype != ST_F32) return 0;
+    size_t tb = st_rope3d_table_bytes(T, H, W, rope_split);
+    if (tb == 0) return 0;
+    size_t n = (size_t)T * H * W;
+    return tb + align_up(n * heads * d * elem_size(dtype), kWsAlign);
+}
+
+st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                                 int heads, int d, const int rope_split[3], float theta,
+                                 st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
+                                 hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, 0, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!workspace) return ST_ERR_NULL;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    if (dtype == ST_F32 && ((long long)H * W > 65535 || T > 65535)) return ST_ERR_SHAPE;
+    size_t need = st_attn_factorized_workspace_bytes(T, H, W, heads, d, rope_split, dtype);
+    if (need == 0) return ST_ERR_SHAPE;
+    if (ws_bytes < need) return ST_ERR_WORKSPACE;
+    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
+    if (overlaps(workspace, ws_bytes, out, bytes) || overlaps(workspace, ws_bytes, q, bytes) ||
+        overlaps(workspace, ws_bytes, k, bytes) || overlaps(workspace, ws_bytes, v, bytes))
+        return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    float2* table = (float2*)workspace;
+    void* o_s = (char*)workspace + table_bytes_for(T, H, W, rope_split);
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    const int S = H * W;
+    if (dtype == ST_BF16) {
+        e = st::launch_attn_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                 (uint16_t*)o_s, table, g, (int)n, heads, S, T, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k,
+                                          (const uint16_t*)o_s, (uint16_t*)out, table, g, heads,
+                                          stream);
+    } else {
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)o_s,
+                                table, g, heads, d, T, S, S, 1, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)o_s, (float*)out,
+                                table, g, heads, d, S, T, 1, S, stream);
+    }
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_text, int heads,
+                          int d, const int rope_split[3], float theta, st_dtype dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!x || !y || !rope_split || !workspace) return ST_ERR_NULL;
+    long long n = 0;
+    if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
+    if (heads < 1 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
+    st_status s = check_split(rope_split, d);
+    if (s != ST_OK) return s;
+    if (dtype == ST_BF16) {
+        if (d % 8) return ST_ERR_UNSUPPORTED;
+    } else if (dtype != ST_F32) {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(y, 16)) return ST_ERR_ALIGN;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    if (ws_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
+    if (x != y && overlaps(x, bytes, y, bytes)) return ST_ERR_ALIAS;
+    if (overlaps(workspace, ws_bytes, x, bytes) || overlaps(workspace, ws_bytes, y, bytes))
+        return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    float2* table = (float2*)workspace;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dtype == ST_BF16)
+        e = st::launch_rope_apply_bf16((const uint16_t*)x, (uint16_t*)y, g, (int)n, heads, d,
+                                       table, stream);
+    else
+        e = st::launch_rope_apply_f32((const float*)x, (float*)y, g, (int)n, heads, d, table,
+                                      stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+const char* st_status_str(st_status s) {
+    switch (s) {
+        case ST_OK: return "ok";
+        case ST_ERR_NULL: return "null pointer";
+        case ST_ERR_SHAPE: return "shape out of range";
+        case ST_ERR_SPLIT: return "invalid rope_split";
+        case ST_ERR_UNSUPPORTED: return "unsupported argument combination";
+        case ST_ERR_WORKSPACE: return "workspace too small";
+        case ST_ERR_HIP: return "HIP launch failed";
+        case ST_ERR_ALIAS: return "output overlaps an input";
+        case ST_ERR_ALIGN: return "pointer misaligned";
+    }
+    return "unknown status";
+}
+
+int st_last_hip_error(void) { return g_last_hip_error; }
+
+const char* st_version(void) { return "0.1.0"; }
+
+}  // extern "C"

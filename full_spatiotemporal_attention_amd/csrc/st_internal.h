@@ -1,0 +1,119 @@
+// Internal declarations shared by the HIP sources of libstattn (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace st {
+
+// ------------------------------------------------------------------------------------------
+// Geometry of the token grid and of the RoPE angle table.
+//
+// Flat token order: n = (t * H + h) * W + w for n < Nv = T*H*W; rows n >= Nv are text rows.
+// Angle table (float2 = cos, sin), built in fp64 and stored as fp32:
+//   [T][pairs[0]] at off[0] = 0, [H][pairs[1]] at off[1], [W][pairs[2]] at off[2], then the
+//   identity entry (1, 0) at `identity`.  Entry for axis a, position p, pair j:
+//   off[a] + p * pairs[a] + j, angle p * theta^(-2j / (2 * pairs[a])).
+// ------------------------------------------------------------------------------------------
+struct RopeGeom {
+    int T, H, W;
+    int S;            // H * W, tokens per frame
+    int Nv;           // T * H * W, video rows
+    float inv_S;      // fp32 reciprocals used by the exact position decode below
+    float inv_W;
+    int pairs[3];     // rotation pairs per axis (t, h, w)
+    int first[3];     // first pair index of each axis inside the head: 0, P_t, P_t + P_h
+    int off[3];       // table offset (entries) of each axis block
+    int identity;     // index of the (1, 0) entry; table size is identity + 1
+};
+
+// Host-side construction (defined in st_attn.cpp).
+RopeGeom make_geom(int T, int H, int W, const int split[3]);
+
+// Exact (t, h, w) of a video row.  n < 2^24 keeps float(n) exact; fl(n * fl(1/S)) is then off
+// from n / S by less than one, so one correction step gives the exact quotient.
+__device__ __forceinline__ void decode_pos(int n, const RopeGeom& g, int& t, int& h, int& w) {
+    int q = (int)((float)n * g.inv_S);
+    int r = n - q * g.S;
+    if (r < 0) { q -= 1; r += g.S; } else if (r >= g.S) { q += 1; r -= g.S; }
+    int qh = (int)((float)r * g.inv_W);
+    int rw = r - qh * g.W;
+    if (rw < 0) { qh -= 1; rw += g.W; } else if (rw >= g.W) { qh += 1; rw -= g.W; }
+    t = q; h = qh; w = rw;
+}
+
+// Table entry of head pair `p` (0 .. d/2-1) for a row at (t, h, w); text rows get the identity.
+__device__ __forceinline__ int pair_entry(int p, int t, int h, int w, bool text, const RopeGeom& g) {
+    int a = (p >= g.first[1]) + (p >= g.first[2]);
+    int j = p - (a == 0 ? 0 : (a == 1 ? g.first[1] : g.first[2]));
+    int pos = a == 0 ? t : (a == 1 ? h : w);
+    int base = a == 0 ? g.off[0] : (a == 1 ? g.off[1] : g.off[2]);
+    int stride = a == 0 ? g.pairs[0] : (a == 1 ? g.pairs[1] : g.pairs[2]);
+    return text ? g.identity : base + pos * stride + j;
+}
+
+// bfloat16 helpers (storage is uint16_t; conversions are exact widening and RNE narrowing).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Two fp32 -> packed bf16x2 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Rotate one pair (x0, x1) by the table entry cs = (cos, sin).
+__device__ __forceinline__ void rotate_pair(float& x0, float& x1, float2 cs) {
+    float y0 = fmaf(x0, cs.x, -x1 * cs.y);
+    float y1 = fmaf(x0, cs.y, x1 * cs.x);
+    x0 = y0; x1 = y1;
+}
+
+// Workgroup remap for 8 XCDs.  Consecutive workgroup ids are dispatched round-robin over the
+// XCDs; this gives each XCD a contiguous range of logical tiles, so tiles that share K/V (same
+// head and segment) run on the same XCD and hit in its L2.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+    const int nx = 8;
+    int x = b % nx, slot = b / nx;
+    int base = total / nx, rem = total % nx;
+    return (x < rem) ? x * (base + 1) + slot : rem * (base + 1) + (x - rem) * base + slot;
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers (one per kernel family).  Each returns hipSuccess or the launch error.
+// ------------------------------------------------------------------------------------------
+
+// Angle table: `table` receives g.identity + 1 float2 entries.
+hipError_t launch_rope_table(const RopeGeom& g, double theta, float2* table, hipStream_t stream);
+
+// Stand-alone rotation, [N][heads][d] bf16 (d % 8 == 0) or fp32 (d even).
+hipError_t launch_rope_apply_bf16(const uint16_t* x, uint16_t* y, const RopeGeom& g, int N,
+                                  int heads, int d, const float2* table, hipStream_t stream);
+hipError_t launch_rope_apply_f32(const float* x, float* y, const RopeGeom& g, int N, int heads,
+                                 int d, const float2* table, hipStream_t stream);
+
+// Flash attention on bf16 MFMA with fused RoPE, d = 128.  Sequences are contiguous row ranges
+// [s * seg_len, (s + 1) * seg_len) for s < n_segs: one segment of N rows for full attention,
+// T segments of H*W rows for the factorised spatial stage.
+hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            uint16_t* out, const float2* table, const RopeGeom& g, int N,
+                            int heads, int seg_len, int n_segs, hipStream_t stream);
+
+// Factorised temporal stage, bf16, d = 128: for each spatial position s and head, the T rows
+// t * S + s attend to each other; values come from `vs` (the spatial stage's output).
+hipError_t launch_attn_temporal_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vs,
+                                     uint16_t* out, const float2* table, const RopeGeom& g,
+                                     int heads, hipStream_t stream);
+
+// fp32 checking kernel over row sets: sequence s holds rows s * base_mul + i * stride,
+// i < seq_len, for s < n_seqs.  Values from `v`, output rows written at the same indices.
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
+                           const float2* table, const RopeGeom& g, int heads, int d,
+                           int n_seqs, int seq_len, int base_mul, int stride, hipStream_t stream);
+
+}  // namespace st

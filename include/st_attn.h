@@ -1,0 +1,148 @@
+/*
+ * st_attn.h -- C ABI of libstattn: 3D-RoPE full spatiotemporal attention (forward) on MI355X.
+ *
+ * What is computed.  A video-DiT self-attention layer sees a T' x H' x W' grid of latent tokens
+ * ("A video model's architecture: spatiotemporal attention and the 3D VAE", self-test answers 1
+ * and 2).  Each head's 128 channels are split into three contiguous ranges rotated by the
+ * token's t, h and w coordinate (same page, self-test answer 4 and "Position: RoPE in three
+ * dimensions"; "CogVideoX Architecture: ...", section "3. 3D Rotary Position Embeddings (3D RoPE)",
+ * the block-diagonal R_3D).  Attention is then non-causal softmax(q~ k~^T / sqrt(d)) v over all
+ * tokens together ("full 3D attention"), or, for the factorised variant, spatial attention inside
+ * each frame followed by temporal attention at each spatial position (first page, "How attention
+ * sees time: factorised or full").
+ *
+ * Conventions shared by every entry point.
+ *   Layout    q, k, v, out, x, y: [N][heads][d] row-major, batch 1, where N = T*H*W + n_text and
+ *             token n < T*H*W sits at t = n / (H*W), h = (n / W) % H, w = n % W (t slowest, w
+ *             fastest).  Rows n >= T*H*W are text tokens: they attend and are attended like any
+ *             token but are not rotated.
+ *   RoPE      rope_split = {d_t, d_h, d_w}: even, >= 0, sum d.  Channels [0, d_t) turn with t,
+ *             [d_t, d_t + d_h) with h, the rest with w.  Inside a range, pair j is channels
+ *             (off + 2j, off + 2j + 1) and turns by pos * theta^(-2j / d_a):
+ *             (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).  V is never rotated.
+ *   Scale     1 / sqrt(d); no mask, no causality.
+ *   dtype     ST_BF16: bfloat16 storage, d == 128, matrix products on bf16 MFMA with fp32
+ *             accumulation, rotated q/k and softmax weights rounded to bf16 before the products,
+ *             fp32 softmax.  ST_F32: float32 storage and arithmetic throughout (a checking mode,
+ *             not a fast path), even d <= 128.
+ *   Memory    Every pointer except rope_split is device memory owned by the caller; the library
+ *             allocates nothing, keeps no global state and is re-entrant.  Tensor pointers must
+ *             be 16-byte aligned, workspace and table pointers 256-byte aligned.  out must not
+ *             overlap q, k or v.
+ *   Streams   All work is enqueued on `stream` (0 = the null stream) and returns without
+ *             waiting for it.  The caller keeps inputs, workspace and outputs alive until the
+ *             stream has run the work.
+ *   Errors    Arguments are checked before anything is enqueued; on an error nothing runs and no
+ *             output or workspace byte is touched.  A failed launch returns ST_ERR_HIP and
+ *             st_last_hip_error() then gives the hipError_t (per calling thread).
+ *   Limits    N < 2^24 rows; T, H, W >= 1; heads >= 1; n_text >= 0; theta finite and > 0.
+ */
+#ifndef ST_ATTN_H
+#define ST_ATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum st_status {
+    ST_OK = 0,
+    ST_ERR_NULL = 1,        /* a required pointer is NULL */
+    ST_ERR_SHAPE = 2,       /* T, H, W, heads, d, n_text or N out of range */
+    ST_ERR_SPLIT = 3,       /* rope_split entries odd, negative or not summing to d */
+    ST_ERR_UNSUPPORTED = 4, /* valid request this build does not serve (dtype/d combination,
+                               text rows on the factorised path, bad theta) */
+    ST_ERR_WORKSPACE = 5,   /* workspace or table smaller than the matching *_bytes() size */
+    ST_ERR_HIP = 6,         /* a kernel launch failed; see st_last_hip_error() */
+    ST_ERR_ALIAS = 7,       /* out overlaps an input */
+    ST_ERR_ALIGN = 8        /* a pointer is not aligned as required */
+} st_status;
+
+typedef enum st_dtype {
+    ST_BF16 = 0,
+    ST_F32 = 1
+} st_dtype;
+
+/* ---------------------------------------------------------------------------------------------
+ * RoPE angle table.  One (cos, sin) float pair per axis position and pair index, built in fp64
+ * and stored as fp32: [T][d_t/2], then [H][d_h/2], then [W][d_w/2], then one identity entry
+ * (1, 0) used by text rows.  Depends only on the grid, the split and theta, so a caller that runs
+ * many layers on one grid can build it once and pass it to st_attn3d_fwd_tabled.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Bytes of the table for this grid and split; 0 if the arguments are invalid. */
+size_t st_rope3d_table_bytes(int T, int H, int W, const int rope_split[3]);
+
+/* Build the table into `table` (device, >= st_rope3d_table_bytes bytes). */
+st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], float theta,
+                                void* table, size_t table_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Full 3D attention: out = softmax(R q . (R k)^T / sqrt(d)) v over all N rows
+ * ("full 3D attention", first page, self-test answer 2 and "How attention sees time").
+ * ------------------------------------------------------------------------------------------- */
+
+/* Workspace bytes st_attn3d_fwd needs (the angle table); 0 if the arguments are invalid. */
+size_t st_attn3d_workspace_bytes(int T, int H, int W, const int rope_split[3]);
+
+/* Build the angle table in `workspace`, then run RoPE-fused attention.  q, k, v, out:
+ * [N][heads][d] of `dtype`.  The workspace is scratch owned by the caller and may be reused
+ * as soon as the stream has run this call. */
+st_status st_attn3d_fwd(const void* q, const void* k, const void* v,
+                        int T, int H, int W, int n_text, int heads, int d,
+                        const int rope_split[3], float theta, st_dtype dtype,
+                        void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+
+/* The same attention with a table already built by st_rope3d_table_build for this grid and
+ * split (read only).  One kernel launch. */
+st_status st_attn3d_fwd_tabled(const void* q, const void* k, const void* v,
+                               int T, int H, int W, int n_text, int heads, int d,
+                               const int rope_split[3], st_dtype dtype,
+                               const void* table, size_t table_bytes, void* out,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Factorised attention (first page, self-test answer 2): stage 1 attends inside each frame
+ * (T sequences of H*W rows), stage 2 attends along time at each spatial position (H*W sequences
+ * of T rows) with the same rotated q and k and stage 1's output as values.  No text rows
+ * (n_text is 0 by construction: N = T*H*W).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Workspace bytes: the angle table plus the stage-1 output [N][heads][d] of `dtype`. */
+size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
+                                          const int rope_split[3], st_dtype dtype);
+
+st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v,
+                                 int T, int H, int W, int heads, int d,
+                                 const int rope_split[3], float theta, st_dtype dtype,
+                                 void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Stand-alone 3D RoPE: y = R_3D(t, h, w) x for every row (text rows copied unchanged).
+ * x and y: [N][heads][d]; y == x (in place) is allowed, other overlaps are not.  ST_BF16 needs
+ * d % 8 == 0, ST_F32 needs d even.  Workspace: st_rope3d_table_bytes bytes.
+ * ------------------------------------------------------------------------------------------- */
+st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_text, int heads,
+                          int d, const int rope_split[3], float theta, st_dtype dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Diagnostics.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Static text naming a status code. */
+const char* st_status_str(st_status s);
+
+/* hipError_t of the last ST_ERR_HIP returned on the calling thread (0 if none). */
+int st_last_hip_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+const char* st_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ST_ATTN_H */

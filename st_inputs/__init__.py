@@ -28,17 +28,21 @@ __all__ = [
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest, ties to even); return the uint16 bits.
 
-    NaN inputs stay NaN (quiet bit set); this is storage conversion only.
+    NaN inputs stay NaN (quiet bit set); this is storage conversion only.  Works in chunks of
+    uint32 arithmetic (finite values cannot carry out of 32 bits).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    rounded = (u + 0x7FFF + lsb) >> 16
-    nan = np.isnan(x)
-    out = rounded.astype(np.uint16)
-    if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
-    return out
+    flat = x.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint16)
+    step = 1 << 24
+    for a in range(0, flat.size, step):
+        u = flat[a:a + step].view(np.uint32)
+        nan = np.isnan(flat[a:a + step])
+        r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+        if nan.any():
+            r[nan] = (u[nan] >> np.uint32(16)) | np.uint32(0x40)
+        out[a:a + step] = r.astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:

@@ -1,0 +1,187 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared symbol, sizes its
+workspaces as documented and rejects invalid arguments before enqueueing anything.
+
+No call here reaches a kernel launch: every argument set below fails validation first (the
+pointer values are never dereferenced by the host code), so these run without a GPU.
+"""
+import os
+import re
+
+import pytest
+
+from full_spatiotemporal_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "st_attn.h")
+
+ST_OK, ST_ERR_NULL, ST_ERR_SHAPE, ST_ERR_SPLIT, ST_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+ST_ERR_WORKSPACE, ST_ERR_HIP, ST_ERR_ALIAS, ST_ERR_ALIGN = 5, 6, 7, 8
+
+# Fake, aligned, non-overlapping "device" addresses: validation never touches them.
+Q, K, V, OUT, WS = 0x100000000, 0x200000000, 0x300000000, 0x400000000, 0x500000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(st_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    try:
+        return _lib.load()
+    except ImportError as e:
+        pytest.skip(str(e))
+
+
+def sp(*s):
+    return _lib.split_arg(s)
+
+
+def test_header_and_binding_agree():
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in range(9):
+        assert lib.st_status_str(code)
+    assert lib.st_status_str(99) == b"unknown status"
+    assert lib.st_version() == b"0.1.0"
+    assert lib.st_last_hip_error() == 0
+
+
+def test_table_bytes(lib):
+    # entries = T*d_t/2 + H*d_h/2 + W*d_w/2 + 1 identity, 8 bytes each, rounded up to 256 B
+    for (t, h, w), split in [((21, 30, 52), (44, 42, 42)), ((33, 45, 80), (16, 56, 56)),
+                             ((3, 4, 6), (44, 42, 42)), ((1, 1, 1), (0, 0, 128))]:
+        entries = t * split[0] // 2 + h * split[1] // 2 + w * split[2] // 2 + 1
+        want = (entries * 8 + 255) // 256 * 256
+        assert lib.st_rope3d_table_bytes(t, h, w, sp(*split)) == want
+        assert lib.st_attn3d_workspace_bytes(t, h, w, sp(*split)) == want
+    assert lib.st_rope3d_table_bytes(0, 4, 6, sp(44, 42, 42)) == 0
+    assert lib.st_rope3d_table_bytes(3, 4, 6, sp(43, 43, 42)) == 0
+    assert lib.st_rope3d_table_bytes(3, 4, 6, None) == 0
+
+
+def test_factorized_workspace_bytes(lib):
+    tb = lib.st_rope3d_table_bytes(21, 30, 52, sp(44, 42, 42))
+    n = 21 * 30 * 52
+    assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 0) == \
+        tb + (n * 12 * 128 * 2 + 255) // 256 * 256
+    assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 1) == \
+        tb + (n * 12 * 128 * 4 + 255) // 256 * 256
+    assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 0, 128, sp(44, 42, 42), 0) == 0
+    assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 7) == 0
+
+
+def fwd(lib, q=Q, k=K, v=V, T=3, H=4, W=6, n_text=0, heads=2, d=128, split=(44, 42, 42),
+        theta=1e4, dtype=0, ws=WS, ws_bytes=1 << 20, out=OUT):
+    return lib.st_attn3d_fwd(q, k, v, T, H, W, n_text, heads, d,
+                             None if split is None else sp(*split), theta, dtype, ws, ws_bytes,
+                             out, None)
+
+
+def test_attn3d_rejects_invalid_arguments(lib):
+    assert fwd(lib, q=None) == ST_ERR_NULL
+    assert fwd(lib, k=None) == ST_ERR_NULL
+    assert fwd(lib, v=None) == ST_ERR_NULL
+    assert fwd(lib, out=None) == ST_ERR_NULL
+    assert fwd(lib, split=None) == ST_ERR_NULL
+    assert fwd(lib, ws=None) == ST_ERR_NULL
+    assert fwd(lib, T=0) == ST_ERR_SHAPE
+    assert fwd(lib, H=-1) == ST_ERR_SHAPE
+    assert fwd(lib, W=0) == ST_ERR_SHAPE
+    assert fwd(lib, n_text=-1) == ST_ERR_SHAPE
+    assert fwd(lib, heads=0) == ST_ERR_SHAPE
+    assert fwd(lib, d=127, split=(43, 42, 42)) == ST_ERR_SHAPE
+    assert fwd(lib, T=256, H=256, W=256) == ST_ERR_SHAPE          # N >= 2^24
+    assert fwd(lib, split=(43, 43, 42)) == ST_ERR_SPLIT
+    assert fwd(lib, split=(44, 42, 40)) == ST_ERR_SPLIT
+    assert fwd(lib, split=(-2, 88, 42)) == ST_ERR_SPLIT
+    assert fwd(lib, d=64, split=(16, 24, 24)) == ST_ERR_UNSUPPORTED  # bf16 needs d = 128
+    assert fwd(lib, d=256, split=(88, 84, 84), dtype=1) == ST_ERR_UNSUPPORTED
+    assert fwd(lib, dtype=5) == ST_ERR_UNSUPPORTED
+    assert fwd(lib, theta=0.0) == ST_ERR_UNSUPPORTED
+    assert fwd(lib, theta=float("nan")) == ST_ERR_UNSUPPORTED
+    assert fwd(lib, theta=-1.0) == ST_ERR_UNSUPPORTED
+    assert fwd(lib, ws_bytes=16) == ST_ERR_WORKSPACE
+    assert fwd(lib, q=Q + 8) == ST_ERR_ALIGN
+    assert fwd(lib, out=OUT + 2) == ST_ERR_ALIGN
+    assert fwd(lib, ws=WS + 16) == ST_ERR_ALIGN
+    assert fwd(lib, out=Q) == ST_ERR_ALIAS
+    assert fwd(lib, out=V + 256) == ST_ERR_ALIAS
+    assert fwd(lib, ws=OUT) == ST_ERR_ALIAS
+    assert lib.st_last_hip_error() == 0
+
+
+def test_tabled_rejects_invalid_arguments(lib):
+    f = lambda **kw: lib.st_attn3d_fwd_tabled(
+        kw.get("q", Q), K, V, 3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, kw.get("table", WS),
+        kw.get("tb", 1 << 16), OUT, None)
+    assert f(q=None) == ST_ERR_NULL
+    assert f(table=None) == ST_ERR_NULL
+    assert f(tb=8) == ST_ERR_WORKSPACE
+    assert f(table=WS + 64) == ST_ERR_ALIGN
+
+
+def test_factorized_rejects_invalid_arguments(lib):
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, T=3, H=4, W=6, heads=2, d=128, split=(44, 42, 42), theta=1e4,
+                 dtype=0, ws=WS, ws_bytes=1 << 24, out=OUT)
+        a.update(kw)
+        return lib.st_attn_factorized_fwd(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"],
+                                          a["heads"], a["d"], sp(*a["split"]), a["theta"],
+                                          a["dtype"], a["ws"], a["ws_bytes"], a["out"], None)
+    assert f(q=None) == ST_ERR_NULL
+    assert f(ws=None) == ST_ERR_NULL
+    assert f(T=0) == ST_ERR_SHAPE
+    assert f(split=(44, 42, 44)) == ST_ERR_SPLIT
+    assert f(d=96, split=(32, 32, 32)) == ST_ERR_UNSUPPORTED
+    assert f(ws_bytes=1024) == ST_ERR_WORKSPACE
+    assert f(dtype=1, H=300, W=300) == ST_ERR_SHAPE                  # fp32 stage-2 grid limit
+    assert f(out=K) == ST_ERR_ALIAS
+    assert f(ws=Q) == ST_ERR_ALIAS
+
+
+def test_rope_apply_rejects_invalid_arguments(lib):
+    def f(**kw):
+        a = dict(x=Q, y=OUT, T=3, H=4, W=6, n_text=0, heads=2, d=128, split=(44, 42, 42),
+                 theta=1e4, dtype=0, ws=WS, ws_bytes=1 << 16)
+        a.update(kw)
+        return lib.st_rope3d_apply(a["x"], a["y"], a["T"], a["H"], a["W"], a["n_text"], a["heads"],
+                                   a["d"], sp(*a["split"]), a["theta"], a["dtype"], a["ws"],
+                                   a["ws_bytes"], None)
+    assert f(x=None) == ST_ERR_NULL
+    assert f(y=None) == ST_ERR_NULL
+    assert f(ws=None) == ST_ERR_NULL
+    assert f(d=126, split=(42, 42, 42)) == ST_ERR_UNSUPPORTED         # bf16 needs d % 8 == 0
+    assert f(split=(44, 44, 42)) == ST_ERR_SPLIT
+    assert f(ws_bytes=8) == ST_ERR_WORKSPACE
+    assert f(y=Q + 256) == ST_ERR_ALIAS
+    assert f(x=Q + 4) == ST_ERR_ALIGN
+    assert f(theta=float("inf")) == ST_ERR_UNSUPPORTED
+
+
+def test_table_build_rejects_invalid_arguments(lib):
+    assert lib.st_rope3d_table_build(3, 4, 6, sp(44, 42, 42), 1e4, None, 4096, None) == ST_ERR_NULL
+    assert lib.st_rope3d_table_build(3, 4, 6, None, 1e4, WS, 4096, None) == ST_ERR_NULL
+    assert lib.st_rope3d_table_build(0, 4, 6, sp(44, 42, 42), 1e4, WS, 4096, None) == ST_ERR_SHAPE
+    assert lib.st_rope3d_table_build(3, 4, 6, sp(45, 41, 42), 1e4, WS, 4096, None) == ST_ERR_SPLIT
+    assert lib.st_rope3d_table_build(3, 4, 6, sp(44, 42, 42), 0.0, WS, 4096, None) == ST_ERR_UNSUPPORTED
+    assert lib.st_rope3d_table_build(3, 4, 6, sp(44, 42, 42), 1e4, WS, 16, None) == ST_ERR_WORKSPACE
+    assert lib.st_rope3d_table_build(3, 4, 6, sp(44, 42, 42), 1e4, WS + 8, 4096, None) == ST_ERR_ALIGN
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import full_spatiotemporal_attention_amd as fa
+    x = torch.zeros(72, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.attn3d(x, x, x, (3, 4, 6))
