@@ -5,10 +5,11 @@ Workload: the 81-frame 832x480 Wan2.1-1.3B-shaped clip, token grid 21 x 30 x 52 
 12 heads, head dim 128, bf16 q/k/v ~ N(0, 1) (seeded, synthetic), RoPE split 44/42/42,
 theta 10000, non-causal full attention, batch 1.
 
-One step = the whole hot path on resident inputs: the RoPE angle table build, then the fused
-RoPE + flash-attention kernel (the two launches st_attn3d_fwd makes, issued as
-st_rope3d_table_build + st_attn3d_fwd_tabled so that HIP events can bracket the attention kernel
-alone).  value = 4 N^2 heads d FLOP per step / wall time per step, in TFLOP/s.
+One step = the whole hot path on resident inputs, exactly what st_attn3d_fwd enqueues: the
+staging step (RoPE angle table, rotated fp16 K tiles, transposed V tiles) and the attention kernel
+(RoPE of Q fused into its load, flash attention on MFMA).  The two halves are issued as
+st_attn3d_stage + st_attn3d_attend so that HIP events on the launch stream can bracket the
+attention kernel alone.  value = 4 N^2 heads d FLOP per step / wall time per step, in TFLOP/s.
 
 Prints one JSON line on stdout (diagnostics go to stderr).
 """
@@ -130,23 +131,23 @@ def main():
                for b in (x.q_bits, x.k_bits, x.v_bits))
     del x
     out = torch.empty_like(q)
-    tb = fa.rope3d_table_bytes(GRID, SPLIT)
-    table = torch.empty(tb, dtype=torch.uint8, device=dev)
+    wsb = fa.attn3d_workspace_bytes(GRID, HEADS, 0, D, SPLIT)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     sp = _lib.split_arg(SPLIT)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
     def step(ev_mid=None):
-        st = lib.st_rope3d_table_build(GRID[0], GRID[1], GRID[2], sp, THETA, table.data_ptr(), tb, sh)
+        st = lib.st_attn3d_stage(k.data_ptr(), v.data_ptr(), GRID[0], GRID[1], GRID[2], 0, HEADS, D,
+                                 sp, THETA, _lib.ST_BF16, ws.data_ptr(), wsb, sh)
         if st:
-            raise _lib.StError("st_rope3d_table_build", st)
+            raise _lib.StError("st_attn3d_stage", st)
         if ev_mid is not None:
             ev_mid.record(stream)
-        st = lib.st_attn3d_fwd_tabled(q.data_ptr(), k.data_ptr(), v.data_ptr(), GRID[0], GRID[1],
-                                      GRID[2], 0, HEADS, D, sp, _lib.ST_BF16, table.data_ptr(), tb,
-                                      out.data_ptr(), sh)
+        st = lib.st_attn3d_attend(q.data_ptr(), GRID[0], GRID[1], GRID[2], 0, HEADS, D, sp,
+                                  _lib.ST_BF16, ws.data_ptr(), wsb, out.data_ptr(), sh)
         if st:
-            raise _lib.StError("st_attn3d_fwd_tabled", st)
+            raise _lib.StError("st_attn3d_attend", st)
 
     for _ in range(args.warmup):
         step()
@@ -169,8 +170,10 @@ def main():
     kern_avg = sum(kern_ms) / len(kern_ms)
     value = flop / (wall_ms * 1e-3) / 1e12
     achieved = flop / (kern_avg * 1e-3) / 1e12
+    stage_ms = [start.elapsed_time(mids[0])] + [ends[i - 1].elapsed_time(mids[i]) for i in range(1, args.steps)]
+    stage_avg = sum(stage_ms) / len(stage_ms)
     eprint(f"step wall {wall_ms:.3f} ms, events {ev_ms:.3f} ms, attention kernel avg {kern_avg:.3f} ms "
-           f"(min {min(kern_ms):.3f}, max {max(kern_ms):.3f})")
+           f"(min {min(kern_ms):.3f}, max {max(kern_ms):.3f}), staging avg {stage_avg:.3f} ms")
 
     result = {
         "metric": "3D-attn fwd TFLOP/s & % bf16 MFMA peak at 21x30x52 tokens, 12 heads, d=128",
@@ -203,6 +206,7 @@ def main():
             "launch_ms": round(kern_avg, 4),
             "flop_per_launch": flop,
         },
+        "stage_ms": round(stage_avg, 4),
     }
 
     if not args.no_extras:
@@ -225,7 +229,7 @@ def main():
         extras["full_over_factorized_flop"] = round(
             flop / (4.0 * GRID[0] * (GRID[1] * GRID[2]) ** 2 * HEADS * D
                     + 4.0 * GRID[1] * GRID[2] * GRID[0] ** 2 * HEADS * D), 3)
-        rws = torch.empty(tb, dtype=torch.uint8, device=dev)
+        rws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
         rout = torch.empty_like(q)
         for _ in range(2):
             fa.rope3d_apply(q, GRID, 0, SPLIT, THETA, out=rout, workspace=rws)
@@ -239,6 +243,18 @@ def main():
         extras["rope_apply_ms"] = round(rope_ms, 4)
         extras["rope_apply_GBps"] = round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1)
         extras["rope_apply_hbm_frac"] = round(rope_bytes / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        # A/B: RoPE of K fused into every tile load (no staging pass), same numerics.
+        fws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            fa.attn3d_fused(q, k, v, GRID, 0, SPLIT, THETA, out=fout, workspace=fws)
+        e0.record(stream)
+        for _ in range(reps):
+            fa.attn3d_fused(q, k, v, GRID, 0, SPLIT, THETA, out=fout, workspace=fws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fused_ms = e0.elapsed_time(e1) / reps
+        extras["fused_rope_step_ms"] = round(fused_ms, 4)
+        extras["fused_rope_TFLOPs"] = round(flop / (fused_ms * 1e-3) / 1e12, 2)
         result["extras"] = extras
         eprint(f"extras: {extras}")
 

@@ -15,7 +15,9 @@ from ._lib import StError  # noqa: F401
 __all__ = [
     "StError",
     "attn3d",
-    "attn3d_tabled",
+    "attn3d_fused",
+    "attn3d_stage",
+    "attn3d_attend",
     "attn_factorized",
     "rope3d_apply",
     "rope3d_table",
@@ -76,9 +78,11 @@ def rope3d_table_bytes(grid, rope_split=WAN_SPLIT) -> int:
     return int(_lib.load().st_rope3d_table_bytes(T, H, W, _lib.split_arg(rope_split)))
 
 
-def attn3d_workspace_bytes(grid, rope_split=WAN_SPLIT) -> int:
+def attn3d_workspace_bytes(grid, heads, n_text=0, d=128, rope_split=WAN_SPLIT,
+                           dtype=torch.bfloat16) -> int:
     T, H, W = (int(x) for x in grid)
-    return int(_lib.load().st_attn3d_workspace_bytes(T, H, W, _lib.split_arg(rope_split)))
+    return int(_lib.load().st_attn3d_workspace_bytes(T, H, W, int(n_text), int(heads), int(d),
+                                                     _lib.split_arg(rope_split), _DTYPES[dtype]))
 
 
 def attn_factorized_workspace_bytes(grid, heads, d=128, rope_split=WAN_SPLIT,
@@ -121,7 +125,7 @@ def attn3d(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
         out = torch.empty_like(q)
     else:
         _check_tensors(grid, n_text, q, out)
-    nbytes = attn3d_workspace_bytes(grid, rope_split)
+    nbytes = attn3d_workspace_bytes(grid, heads, n_text, d, rope_split, q.dtype)
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn3d_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads,
                            d, _lib.split_arg(rope_split), float(theta), _dtype_code(q),
@@ -131,17 +135,50 @@ def attn3d(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
     return out
 
 
-def attn3d_tabled(q, k, v, grid, table, n_text=0, rope_split=WAN_SPLIT, out=None) -> torch.Tensor:
-    """Full 3D attention with an angle table from ``rope3d_table`` (one kernel launch)."""
+def attn3d_fused(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=None,
+                 workspace=None) -> torch.Tensor:
+    """The same attention with K rotated (and V transposed) inside every tile load."""
     lib = _lib.load()
     T, H, W, heads, d = _check_tensors(grid, n_text, q, k, v)
     if out is None:
         out = torch.empty_like(q)
-    st = lib.st_attn3d_fwd_tabled(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
-                                  heads, d, _lib.split_arg(rope_split), _dtype_code(q),
-                                  table.data_ptr(), table.numel() * table.element_size(),
-                                  out.data_ptr(), _stream(q.device))
-    _lib.check("st_attn3d_fwd_tabled", st)
+    else:
+        _check_tensors(grid, n_text, q, out)
+    nbytes = int(lib.st_attn3d_fused_workspace_bytes(T, H, W, _lib.split_arg(rope_split)))
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib.st_attn3d_fwd_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
+                                 heads, d, _lib.split_arg(rope_split), float(theta), _dtype_code(q),
+                                 ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
+                                 _stream(q.device))
+    _lib.check("st_attn3d_fwd_fused", st)
+    return out
+
+
+def attn3d_stage(k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0,
+                 workspace=None) -> torch.Tensor:
+    """First step of the bf16 path: angle table, rotated fp16 K tiles, transposed V tiles."""
+    lib = _lib.load()
+    T, H, W, heads, d = _check_tensors(grid, n_text, k, v)
+    nbytes = attn3d_workspace_bytes(grid, heads, n_text, d, rope_split, k.dtype)
+    ws = _workspace(nbytes, k.device, workspace)
+    st = lib.st_attn3d_stage(k.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads, d,
+                             _lib.split_arg(rope_split), float(theta), _dtype_code(k),
+                             ws.data_ptr(), ws.numel() * ws.element_size(), _stream(k.device))
+    _lib.check("st_attn3d_stage", st)
+    return ws
+
+
+def attn3d_attend(q, grid, workspace, n_text=0, rope_split=WAN_SPLIT, out=None) -> torch.Tensor:
+    """Second step of the bf16 path: attention of q against a staged workspace."""
+    lib = _lib.load()
+    T, H, W, heads, d = _check_tensors(grid, n_text, q)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.st_attn3d_attend(q.data_ptr(), T, H, W, int(n_text), heads, d,
+                              _lib.split_arg(rope_split), _dtype_code(q), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), out.data_ptr(),
+                              _stream(q.device))
+    _lib.check("st_attn3d_attend", st)
     return out
 
 

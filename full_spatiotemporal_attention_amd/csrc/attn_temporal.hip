@@ -1,4 +1,4 @@
-// Temporal stage of factorised attention on bf16 MFMA (gfx950).
+// Temporal stage of factorised attention on MFMA (gfx950), bf16 storage.
 //
 // After spatial attention inside each frame, every spatial position s attends along time: the T
 // rows t * S + s, t < T, form one short sequence ("A video model's architecture: spatiotemporal
@@ -7,7 +7,9 @@
 // 5 to 33 for the pages' grids) and many (H'W' x heads), so the kernel is bound by HBM traffic:
 // each wave owns one (s, head) sequence, keeps its Q~ and K~ blocks in registers and stages only
 // the transposed values through LDS.  Four waves of a workgroup take four consecutive heads of
-// the same position, whose rows are adjacent in memory.
+// the same position, whose rows are adjacent in memory.  Numerics as in the full-attention
+// kernel: rotated q and k in fp16 for the score product, weights in bf16 against the bf16
+// values, fp32 accumulation.
 #include "st_internal.h"
 
 namespace st {
@@ -33,6 +35,10 @@ struct TemporalParams {
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Rotate 8 bf16 channels (pairs 4c .. 4c+3) and return them as fp16 (the score-product type).
 __device__ __forceinline__ uint4 rope_chunk(uint4 raw, int c, int t, int h, int w,
                                             const RopeGeom& g, const float2* __restrict__ table) {
     uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -41,7 +47,8 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 raw, int c, int t, int h, int 
         float2 cs = table[pair_entry(4 * c + i, t, h, w, false, g)];
         float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
         rotate_pair(x0, x1, cs);
-        wd[i] = pack_bf16x2(x0, x1);
+        f16x2_t hv = {(_Float16)x0, (_Float16)x1};
+        wd[i] = __builtin_bit_cast(uint32_t, hv);
     }
     return make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }
@@ -79,14 +86,14 @@ __global__ void __launch_bounds__(WAVES * 64) attn_temporal_bf16_kernel(Temporal
     for (int qb = 0; qb < nblk; ++qb) {
         const int tq = qb * TB + l32;
         const bool qv = tq < T;
-        bf16x8_t qreg[8];
+        f16x8_t qreg[8];
         {
             const uint16_t* qp = p.q + (long long)(tq * S + s) * row_stride + (long long)head * D;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) {
                 int c = 2 * ks + hh;
                 uint4 raw = qv ? ld16(qp + 8 * c) : make_uint4(0, 0, 0, 0);
-                qreg[ks] = __builtin_bit_cast(bf16x8_t, rope_chunk(raw, c, qv ? tq : 0, sh, sw, g, p.table));
+                qreg[ks] = __builtin_bit_cast(f16x8_t, rope_chunk(raw, c, qv ? tq : 0, sh, sw, g, p.table));
             }
         }
         f32x16_t oacc[4];
@@ -108,8 +115,8 @@ __global__ void __launch_bounds__(WAVES * 64) attn_temporal_bf16_kernel(Temporal
                 for (int ks = 0; ks < 8; ++ks) {
                     int c = 2 * ks + hh;
                     uint4 raw = kv ? ld16(kp + 8 * c) : make_uint4(0, 0, 0, 0);
-                    bf16x8_t a = __builtin_bit_cast(bf16x8_t, rope_chunk(raw, c, kv ? tk : 0, sh, sw, g, p.table));
-                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], sacc, 0, 0, 0);
+                    f16x8_t a = __builtin_bit_cast(f16x8_t, rope_chunk(raw, c, kv ? tk : 0, sh, sw, g, p.table));
+                    sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], sacc, 0, 0, 0);
                 }
             }
             // values of this key block -> LDS, transposed (keys within 16: 0-3, 8-11, 4-7, 12-15)

@@ -85,6 +85,7 @@ st_status check_attn(const void* q, const void* k, const void* v, const void* ou
     if (!split) return ST_ERR_NULL;
     long long n = 0;
     if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
+    *n_out = n;
     if (heads < 1 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
     if ((long long)n * heads * d >= (1LL << 40)) return ST_ERR_SHAPE;
     st_status s = check_split(split, d);
@@ -103,7 +104,6 @@ st_status check_attn(const void* q, const void* k, const void* v, const void* ou
     if (overlaps(out, bytes, q, bytes) || overlaps(out, bytes, k, bytes) ||
         overlaps(out, bytes, v, bytes))
         return ST_ERR_ALIAS;
-    *n_out = n;
     return ST_OK;
 }
 
@@ -112,15 +112,27 @@ st_status hip_fail(hipError_t e) {
     return ST_ERR_HIP;
 }
 
-// Launch the attention kernels for one of the two modes, given a built table.
-hipError_t run_full(const void* q, const void* k, const void* v, void* out, const st::RopeGeom& g,
-                    int n, int heads, int d, st_dtype dtype, const float2* table,
-                    hipStream_t stream) {
-    if (dtype == ST_BF16)
-        return st::launch_attn_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                    (uint16_t*)out, table, g, n, heads, n, 1, stream);
-    return st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out,
-                               table, g, heads, d, 1, n, 0, 1, stream);
+// Byte layout of the bf16 staged workspace: [table][K~ tiles][V^T tiles], each 256-aligned.
+struct StageLayout {
+    size_t table_bytes;
+    size_t tiles_bytes;   // one of the two tile arrays
+    size_t total;
+};
+
+StageLayout stage_layout(int T, int H, int W, int heads, int seg_len, int n_segs, const int* split) {
+    StageLayout L;
+    L.table_bytes = table_bytes_for(T, H, W, split);
+    L.tiles_bytes = align_up(st::attn_stage_elems(heads, seg_len, n_segs) * 2, kWsAlign);
+    L.total = L.table_bytes + 2 * L.tiles_bytes;
+    return L;
+}
+
+bool ws_overlaps_tensors(const void* ws, size_t ws_bytes, size_t tensor_bytes, const void* a,
+                         const void* b, const void* c, const void* d) {
+    const void* ts[4] = {a, b, c, d};
+    for (const void* t : ts)
+        if (t && overlaps(ws, ws_bytes, t, tensor_bytes)) return true;
+    return false;
 }
 
 }  // namespace
@@ -148,22 +160,65 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
-size_t st_attn3d_workspace_bytes(int T, int H, int W, const int rope_split[3]) {
+size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
+                                 const int rope_split[3], st_dtype dtype) {
+    long long n = 0;
+    if (!rope_split || !grid_ok(T, H, W, n_text, &n) || heads < 1) return 0;
+    if (check_split(rope_split, d) != ST_OK) return 0;
+    if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) : 0;
+    if (dtype != ST_BF16 || d != 128) return 0;
+    return stage_layout(T, H, W, heads, (int)n, 1, rope_split).total;
+}
+
+size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split[3]) {
     return st_rope3d_table_bytes(T, H, W, rope_split);
 }
 
-st_status st_attn3d_fwd_tabled(const void* q, const void* k, const void* v, int T, int H, int W,
-                               int n_text, int heads, int d, const int rope_split[3],
-                               st_dtype dtype, const void* table, size_t table_bytes, void* out,
-                               hipStream_t stream) {
+st_status st_attn3d_stage(const void* k, const void* v, int T, int H, int W, int n_text, int heads,
+                          int d, const int rope_split[3], float theta, st_dtype dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
     long long n = 0;
-    st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    // q is not read by this step; pass k in its place for the shared checks.
+    st_status s = check_attn(k, k, v, workspace, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s == ST_ERR_ALIAS) s = ST_OK;  // workspace aliasing is checked below with its true size
     if (s != ST_OK) return s;
-    if (!table) return ST_ERR_NULL;
-    if (!aligned(table, kWsAlign)) return ST_ERR_ALIGN;
-    if (table_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    if (dtype != ST_BF16) return ST_ERR_UNSUPPORTED;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    StageLayout L = stage_layout(T, H, W, heads, (int)n, 1, rope_split);
+    if (ws_bytes < L.total) return ST_ERR_WORKSPACE;
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, k, v, nullptr, nullptr))
+        return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
-    hipError_t e = run_full(q, k, v, out, g, (int)n, heads, d, dtype, (const float2*)table, stream);
+    char* ws = (char*)workspace;
+    float2* table = (float2*)ws;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = st::launch_kv_prep((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(ws + L.table_bytes),
+                           (uint16_t*)(ws + L.table_bytes + L.tiles_bytes), table, g, heads, (int)n, 1,
+                           stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+st_status st_attn3d_attend(const void* q, int T, int H, int W, int n_text, int heads, int d,
+                           const int rope_split[3], st_dtype dtype, const void* workspace,
+                           size_t ws_bytes, void* out, hipStream_t stream) {
+    long long n = 0;
+    if (!workspace) return ST_ERR_NULL;
+    st_status s = check_attn(q, q, q, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (dtype != ST_BF16) return ST_ERR_UNSUPPORTED;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    StageLayout L = stage_layout(T, H, W, heads, (int)n, 1, rope_split);
+    if (ws_bytes < L.total) return ST_ERR_WORKSPACE;
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, q, out, nullptr, nullptr))
+        return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    const char* ws = (const char*)workspace;
+    hipError_t e = st::launch_attn_bf16_staged(
+        (const uint16_t*)q, (const uint16_t*)(ws + L.table_bytes),
+        (const uint16_t*)(ws + L.table_bytes + L.tiles_bytes), (uint16_t*)out, (const float2*)ws, g,
+        heads, (int)n, 1, stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -177,27 +232,62 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int 
     if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
     if (!workspace) return ST_ERR_NULL;
     if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    if (ws_bytes < st_attn3d_workspace_bytes(T, H, W, n_text, heads, d, rope_split, dtype))
+        return ST_ERR_WORKSPACE;
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * elem_size(dtype), q, k, v, out))
+        return ST_ERR_ALIAS;
+    if (dtype == ST_BF16) {
+        s = st_attn3d_stage(k, v, T, H, W, n_text, heads, d, rope_split, theta, dtype, workspace,
+                            ws_bytes, stream);
+        if (s != ST_OK) return s;
+        return st_attn3d_attend(q, T, H, W, n_text, heads, d, rope_split, dtype, workspace, ws_bytes,
+                                out, stream);
+    }
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    float2* table = (float2*)workspace;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, table, g,
+                            heads, d, 1, (int)n, 0, 1, stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T, int H, int W,
+                              int n_text, int heads, int d, const int rope_split[3], float theta,
+                              st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
+                              hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!workspace) return ST_ERR_NULL;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
     if (ws_bytes < table_bytes_for(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
-    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
-    if (overlaps(workspace, ws_bytes, out, bytes) || overlaps(workspace, ws_bytes, q, bytes) ||
-        overlaps(workspace, ws_bytes, k, bytes) || overlaps(workspace, ws_bytes, v, bytes))
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * elem_size(dtype), q, k, v, out))
         return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
     float2* table = (float2*)workspace;
     hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
     if (e != hipSuccess) return hip_fail(e);
-    e = run_full(q, k, v, out, g, (int)n, heads, d, dtype, table, stream);
+    if (dtype == ST_BF16)
+        e = st::launch_attn_bf16_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                       (uint16_t*)out, table, g, heads, (int)n, 1, stream);
+    else
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, table,
+                                g, heads, d, 1, (int)n, 0, 1, stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
 size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
                                           const int rope_split[3], st_dtype dtype) {
     if (!rope_split || heads < 1 || d < 2 || (d & 1)) return 0;
-    if (dtype != ST_BF16 && dtype != ST_F32) return 0;
-    size_t tb = st_rope3d_table_bytes(T, H, W, rope_split);
-    if (tb == 0) return 0;
-    size_t n = (size_t)T * H * W;
-    return tb + align_up(n * heads * d * elem_size(dtype), kWsAlign);
+    long long n = 0;
+    if (!grid_ok(T, H, W, 0, &n)) return 0;
+    if (check_split(rope_split, d) != ST_OK) return 0;
+    size_t os = align_up((size_t)n * heads * d * elem_size(dtype), kWsAlign);
+    if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) + os : 0;
+    if (dtype != ST_BF16 || d != 128) return 0;
+    return stage_layout(T, H, W, heads, H * W, T, rope_split).total + os;
 }
 
 st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
@@ -214,29 +304,33 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
     size_t need = st_attn_factorized_workspace_bytes(T, H, W, heads, d, rope_split, dtype);
     if (need == 0) return ST_ERR_SHAPE;
     if (ws_bytes < need) return ST_ERR_WORKSPACE;
-    size_t bytes = (size_t)n * heads * d * elem_size(dtype);
-    if (overlaps(workspace, ws_bytes, out, bytes) || overlaps(workspace, ws_bytes, q, bytes) ||
-        overlaps(workspace, ws_bytes, k, bytes) || overlaps(workspace, ws_bytes, v, bytes))
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * elem_size(dtype), q, k, v, out))
         return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
-    float2* table = (float2*)workspace;
-    void* o_s = (char*)workspace + table_bytes_for(T, H, W, rope_split);
+    char* ws = (char*)workspace;
+    float2* table = (float2*)ws;
+    const int S = H * W;
     hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
     if (e != hipSuccess) return hip_fail(e);
-    const int S = H * W;
     if (dtype == ST_BF16) {
-        e = st::launch_attn_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                 (uint16_t*)o_s, table, g, (int)n, heads, S, T, stream);
+        StageLayout L = stage_layout(T, H, W, heads, S, T, rope_split);
+        uint16_t* kt = (uint16_t*)(ws + L.table_bytes);
+        uint16_t* vt = (uint16_t*)(ws + L.table_bytes + L.tiles_bytes);
+        uint16_t* o_s = (uint16_t*)(ws + L.total);
+        e = st::launch_kv_prep((const uint16_t*)k, (const uint16_t*)v, kt, vt, table, g, heads, S, T,
+                               stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k,
-                                          (const uint16_t*)o_s, (uint16_t*)out, table, g, heads,
-                                          stream);
+        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, vt, o_s, table, g, heads, S, T, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, o_s, (uint16_t*)out,
+                                          table, g, heads, stream);
     } else {
-        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)o_s,
-                                table, g, heads, d, T, S, S, 1, stream);
+        float* o_s = (float*)(ws + table_bytes_for(T, H, W, rope_split));
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, o_s, table, g,
+                                heads, d, T, S, S, 1, stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)o_s, (float*)out,
-                                table, g, heads, d, S, T, 1, S, stream);
+        e = st::launch_attn_f32((const float*)q, (const float*)k, o_s, (float*)out, table, g, heads,
+                                d, S, T, 1, S, stream);
     }
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }

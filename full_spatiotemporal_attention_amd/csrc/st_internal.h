@@ -27,7 +27,7 @@ struct RopeGeom {
     int identity;     // index of the (1, 0) entry; table size is identity + 1
 };
 
-// Host-side construction (defined in st_attn.cpp).
+// Host-side construction (defined in st_api.hip).
 RopeGeom make_geom(int T, int H, int W, const int split[3]);
 
 // Exact (t, h, w) of a video row.  n < 2^24 keeps float(n) exact; fl(n * fl(1/S)) is then off
@@ -97,12 +97,23 @@ hipError_t launch_rope_apply_bf16(const uint16_t* x, uint16_t* y, const RopeGeom
 hipError_t launch_rope_apply_f32(const float* x, float* y, const RopeGeom& g, int N, int heads,
                                  int d, const float2* table, hipStream_t stream);
 
-// Flash attention on bf16 MFMA with fused RoPE, d = 128.  Sequences are contiguous row ranges
+// Flash attention for bf16 storage, d = 128.  Sequences are contiguous row ranges
 // [s * seg_len, (s + 1) * seg_len) for s < n_segs: one segment of N rows for full attention,
 // T segments of H*W rows for the factorised spatial stage.
-hipError_t launch_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                            uint16_t* out, const float2* table, const RopeGeom& g, int N,
-                            int heads, int seg_len, int n_segs, hipStream_t stream);
+//
+// Staged mode: launch_kv_prep rotates K into fp16 tiles `kt` and transposes V into tiles `vt`
+// (attn_stage_elems(...) uint16 elements each), then launch_attn_bf16_staged reads them.
+// Fused mode: launch_attn_bf16_fused reads K and V directly and rotates K on every tile load.
+size_t attn_stage_elems(int heads, int seg_len, int n_segs);
+hipError_t launch_kv_prep(const uint16_t* k, const uint16_t* v, uint16_t* kt, uint16_t* vt,
+                          const float2* table, const RopeGeom& g, int heads, int seg_len,
+                          int n_segs, hipStream_t stream);
+hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* vt,
+                                   uint16_t* out, const float2* table, const RopeGeom& g,
+                                   int heads, int seg_len, int n_segs, hipStream_t stream);
+hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                  uint16_t* out, const float2* table, const RopeGeom& g,
+                                  int heads, int seg_len, int n_segs, hipStream_t stream);
 
 // Factorised temporal stage, bf16, d = 128: for each spatial position s and head, the T rows
 // t * S + s attend to each other; values come from `vs` (the spatial stage's output).

@@ -21,10 +21,11 @@
  *             (off + 2j, off + 2j + 1) and turns by pos * theta^(-2j / d_a):
  *             (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).  V is never rotated.
  *   Scale     1 / sqrt(d); no mask, no causality.
- *   dtype     ST_BF16: bfloat16 storage, d == 128, matrix products on bf16 MFMA with fp32
- *             accumulation, rotated q/k and softmax weights rounded to bf16 before the products,
- *             fp32 softmax.  ST_F32: float32 storage and arithmetic throughout (a checking mode,
- *             not a fast path), even d <= 128.
+ *   dtype     ST_BF16: bfloat16 storage, d == 128; matrix products on MFMA with fp32
+ *             accumulation: rotated q/k rounded to fp16 for the scores, softmax weights rounded
+ *             to bf16 for the product with v; fp32 softmax; output rounded to bf16.
+ *             ST_F32: float32 storage and arithmetic throughout (a checking mode, not a fast
+ *             path), even d <= 128.
  *   Memory    Every pointer except rope_split is device memory owned by the caller; the library
  *             allocates nothing, keeps no global state and is re-entrant.  Tensor pointers must
  *             be 16-byte aligned, workspace and table pointers 256-byte aligned.  out must not
@@ -69,7 +70,8 @@ typedef enum st_dtype {
  * RoPE angle table.  One (cos, sin) float pair per axis position and pair index, built in fp64
  * and stored as fp32: [T][d_t/2], then [H][d_h/2], then [W][d_w/2], then one identity entry
  * (1, 0) used by text rows.  Depends only on the grid, the split and theta, so a caller that runs
- * many layers on one grid can build it once and pass it to st_attn3d_fwd_tabled.
+ * many layers on one grid can build it once.  The attention entry points build their own copy
+ * in their workspace.
  * ------------------------------------------------------------------------------------------- */
 
 /* Bytes of the table for this grid and split; 0 if the arguments are invalid. */
@@ -82,26 +84,53 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
 /* ---------------------------------------------------------------------------------------------
  * Full 3D attention: out = softmax(R q . (R k)^T / sqrt(d)) v over all N rows
  * ("full 3D attention", first page, self-test answer 2 and "How attention sees time").
+ *
+ * ST_BF16 runs in two steps, both on `stream`:
+ *   stage:  the angle table, the rotated K rows as fp16 tiles and the V rows transposed into
+ *           tiles, all written into the caller's workspace (one pass over K and V);
+ *   attend: the attention kernel; it rotates Q itself and streams the staged K/V tiles.
+ * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
+ * fp16 for the score product, so every rotated q/k entry must stay below 65504 in magnitude
+ * (inputs with |x| < 2^15 are always safe); softmax weights multiply V in bf16.
+ * ST_F32 runs one fp32 kernel; its workspace is the angle table only.
  * ------------------------------------------------------------------------------------------- */
 
-/* Workspace bytes st_attn3d_fwd needs (the angle table); 0 if the arguments are invalid. */
-size_t st_attn3d_workspace_bytes(int T, int H, int W, const int rope_split[3]);
+/* Workspace bytes st_attn3d_fwd (and stage/attend) need; 0 if the arguments are invalid.
+ * ST_BF16: table + 2 x heads x ceil(N/64) x 64 x d x 2 bytes; ST_F32: table. */
+size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
+                                 const int rope_split[3], st_dtype dtype);
 
-/* Build the angle table in `workspace`, then run RoPE-fused attention.  q, k, v, out:
- * [N][heads][d] of `dtype`.  The workspace is scratch owned by the caller and may be reused
- * as soon as the stream has run this call. */
+/* q, k, v, out: [N][heads][d] of `dtype`.  The workspace is scratch owned by the caller and may
+ * be reused as soon as the stream has run this call. */
 st_status st_attn3d_fwd(const void* q, const void* k, const void* v,
                         int T, int H, int W, int n_text, int heads, int d,
                         const int rope_split[3], float theta, st_dtype dtype,
                         void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
-/* The same attention with a table already built by st_rope3d_table_build for this grid and
- * split (read only).  One kernel launch. */
-st_status st_attn3d_fwd_tabled(const void* q, const void* k, const void* v,
-                               int T, int H, int W, int n_text, int heads, int d,
-                               const int rope_split[3], st_dtype dtype,
-                               const void* table, size_t table_bytes, void* out,
-                               hipStream_t stream);
+/* First step of the ST_BF16 path: fill `workspace` from k and v.  ST_F32 is not served here
+ * (ST_ERR_UNSUPPORTED). */
+st_status st_attn3d_stage(const void* k, const void* v,
+                          int T, int H, int W, int n_text, int heads, int d,
+                          const int rope_split[3], float theta, st_dtype dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* Second step of the ST_BF16 path: attention of q against a workspace that st_attn3d_stage
+ * filled for the same grid, n_text, heads, d and rope_split (read only).  One kernel launch. */
+st_status st_attn3d_attend(const void* q, int T, int H, int W, int n_text, int heads, int d,
+                           const int rope_split[3], st_dtype dtype,
+                           const void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+
+/* Workspace bytes of st_attn3d_fwd_fused: the angle table only. */
+size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split[3]);
+
+/* The same result with RoPE fused into the attention kernel's tile loads: every K tile is
+ * rotated (position decoded from its flat row index) and every V tile transposed while it is
+ * copied into LDS, with no staging pass.  Two launches (table, attention).  ST_F32 runs the
+ * fp32 kernel as st_attn3d_fwd does. */
+st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
+                              int T, int H, int W, int n_text, int heads, int d,
+                              const int rope_split[3], float theta, st_dtype dtype,
+                              void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Factorised attention (first page, self-test answer 2): stage 1 attends inside each frame
@@ -110,7 +139,8 @@ st_status st_attn3d_fwd_tabled(const void* q, const void* k, const void* v,
  * (n_text is 0 by construction: N = T*H*W).
  * ------------------------------------------------------------------------------------------- */
 
-/* Workspace bytes: the angle table plus the stage-1 output [N][heads][d] of `dtype`. */
+/* Workspace bytes: the angle table, for ST_BF16 the staged K/V tiles of the per-frame sequences
+ * (as for st_attn3d_fwd), and the stage-1 output [N][heads][d] of `dtype`. */
 size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
                                           const int rope_split[3], st_dtype dtype);
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 import full_spatiotemporal_attention_amd as fa
 from st_inputs import make_qkv, sample_rows
-from parity_util import assert_close, host_f64, log, to_device
+from parity_util import assert_close, errors, host_f64, log, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -135,23 +135,47 @@ def test_full_f32_small(grid, n_text, heads, split):
 
 
 def test_stress_value_offset_and_peaky_queries():
-    # v + 10 exposes normalisation error as 10 dl / l; q x 8 makes the softmax peaky.
+    # v + 10 exposes normalisation error as 10 dl / l.  Outputs near 10 are stored in bf16 with a
+    # spacing of 2^-4, so the element bound adds the output rounding (2^-9 relative) to 2e-2;
+    # relative L2 keeps the 5e-3 bar.  q x 8 makes the softmax peaky.
     got, ref = run_full((5, 9, 11), 2, "bf16", 300, v_offset=10.0)
-    assert_close(got - 10.0, ref - 10.0, "bf16", "v+10 (offset removed)")
-    assert_close(got, ref, "bf16", "v+10")
+    assert np.isfinite(got).all()
+    _, rel = errors(got, ref)
+    log(f"    v+10: rel_l2={rel:.3e}")
+    assert rel <= 5e-3
+    assert (np.abs(got - ref) <= 2e-2 + np.abs(ref) * 2.0 ** -9).all()
     got, ref = run_full((5, 9, 11), 2, "bf16", 301, q_mult=8.0)
     assert_close(got, ref, "bf16", "q*8")
 
 
-def test_tabled_matches_fwd_bitwise():
+def test_stage_attend_matches_fwd_bitwise():
     grid, heads = (5, 9, 11), 2
     x = make_qkv(495, heads, 128, 400, "bf16")
     q, k, v = to_device(x)
     a = fa.attn3d(q, k, v, grid)
-    tab = fa.rope3d_table(grid)
-    b = fa.attn3d_tabled(q, k, v, grid, tab)
+    ws = fa.attn3d_stage(k, v, grid)
+    b = fa.attn3d_attend(q, grid, ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("grid,n_text,heads,split", [
+    ((3, 5, 7), 0, 2, WAN), ((7, 11, 13), 0, 2, WAN), ((2, 3, 4), 5, 3, HUN), ((1, 1, 1), 300, 2, WAN),
+])
+def test_fused_rope_path(grid, n_text, heads, split):
+    # K rotated on every tile load instead of a staging pass: same numerics (fp16 rotated K),
+    # so the outputs agree bit for bit with the staged path, and with the oracle to tolerance.
+    T, H, W = grid
+    n = T * H * W + n_text
+    log(f"  fused rope grid={grid} n_text={n_text} heads={heads}")
+    x = make_qkv(n, heads, 128, 450 + n, "bf16")
+    q, k, v = to_device(x)
+    a = fa.attn3d_fused(q, k, v, grid, n_text=n_text, rope_split=split)
+    b = fa.attn3d(q, k, v, grid, n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, grid, n_text, split)
+    assert_close(host_f64(a), ref, "bf16", f"fused {grid}+{n_text}")
 
 
 def test_deterministic():
