@@ -154,27 +154,27 @@ def attn3d_fused(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, o
     return out
 
 
-def attn3d_stage(k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0,
+def attn3d_stage(k, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0,
                  workspace=None) -> torch.Tensor:
-    """First step of the bf16 path: angle table, rotated fp16 K tiles, transposed V tiles."""
+    """First step of the bf16 path: angle table and rotated fp16 K tiles in a workspace."""
     lib = _lib.load()
-    T, H, W, heads, d = _check_tensors(grid, n_text, k, v)
+    T, H, W, heads, d = _check_tensors(grid, n_text, k)
     nbytes = attn3d_workspace_bytes(grid, heads, n_text, d, rope_split, k.dtype)
     ws = _workspace(nbytes, k.device, workspace)
-    st = lib.st_attn3d_stage(k.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads, d,
+    st = lib.st_attn3d_stage(k.data_ptr(), T, H, W, int(n_text), heads, d,
                              _lib.split_arg(rope_split), float(theta), _dtype_code(k),
                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(k.device))
     _lib.check("st_attn3d_stage", st)
     return ws
 
 
-def attn3d_attend(q, grid, workspace, n_text=0, rope_split=WAN_SPLIT, out=None) -> torch.Tensor:
-    """Second step of the bf16 path: attention of q against a staged workspace."""
+def attn3d_attend(q, v, grid, workspace, n_text=0, rope_split=WAN_SPLIT, out=None) -> torch.Tensor:
+    """Second step of the bf16 path: attention of q against a staged workspace, values v."""
     lib = _lib.load()
-    T, H, W, heads, d = _check_tensors(grid, n_text, q)
+    T, H, W, heads, d = _check_tensors(grid, n_text, q, v)
     if out is None:
         out = torch.empty_like(q)
-    st = lib.st_attn3d_attend(q.data_ptr(), T, H, W, int(n_text), heads, d,
+    st = lib.st_attn3d_attend(q.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads, d,
                               _lib.split_arg(rope_split), _dtype_code(q), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), out.data_ptr(),
                               _stream(q.device))

@@ -28,8 +28,8 @@ SIGNATURES = {
     "st_rope3d_table_build": (_i, [_i, _i, _i, _split, _f, _p, _sz, _p]),
     "st_attn3d_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _split, _i]),
     "st_attn3d_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p]),
-    "st_attn3d_stage": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p]),
-    "st_attn3d_attend": (_i, [_p, _i, _i, _i, _i, _i, _i, _split, _i, _p, _sz, _p, _p]),
+    "st_attn3d_stage": (_i, [_p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p]),
+    "st_attn3d_attend": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _split, _i, _p, _sz, _p, _p]),
     "st_attn3d_fused_workspace_bytes": (_sz, [_i, _i, _i, _split]),
     "st_attn3d_fwd_fused": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p]),
     "st_attn_factorized_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _split, _i]),

@@ -22,6 +22,14 @@ ARCH = "gfx950"
 
 SOURCES = ["st_api.hip", "rope.hip", "attn_bf16.hip", "attn_temporal.hip", "attn_f32.hip"]
 
+# Extra flags per source.  The flash kernels take row maxima of MFMA results with fmaxf; without
+# -fno-honor-nans every operand is first canonicalised (an extra v_max_f32 x, x each).  A NaN
+# input still reaches the output: it enters the exponentials and the products.
+SOURCE_FLAGS = {
+    "attn_bf16.hip": ["-fno-honor-nans"],
+    "attn_temporal.hip": ["-fno-honor-nans"],
+}
+
 # Packed fp32 instructions are switched off for all device code (the compiler would otherwise
 # form v_pk_{add,mul,fma}_f32 from scalar float code).
 HIPCC_FLAGS = [
@@ -47,7 +55,8 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

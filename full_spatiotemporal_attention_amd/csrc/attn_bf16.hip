@@ -12,27 +12,34 @@
 // the exact bf16 values (v_mfma_f32_32x32x16_bf16); accumulation, the running max and the row
 // sums are fp32, and the row sum adds exactly the rounded weights the product used.
 //
-// Two ways to feed K and V (template flag FUSED):
-//  * FUSED: K and V tiles are read from the caller's [N][heads][128] tensors; every K tile is
-//    rotated (position decoded from the flat row index) while it is copied into LDS, and every V
-//    tile is transposed on the same copy.  Nothing else runs before the kernel.
-//  * staged (default): a preparation kernel first rotates K into fp16 tiles and transposes V into
-//    the V^T tile order, once per key; the attention kernel then copies tiles without arithmetic.
-//    Q is rotated inside the attention kernel in both modes (once per workgroup).
+// How K reaches the kernel (template flag FUSED):
+//  * staged (default): a preparation kernel rotates K once per key into fp16 tiles
+//    [head][segment][tile][64][128]; the attention kernel copies them into LDS untouched.
+//  * FUSED: K tiles are read from the caller's [N][heads][128] tensor and rotated (position
+//    decoded from the flat row index) on every tile load, through registers.
+// Q is rotated inside the attention kernel in both modes (once per workgroup); V is never
+// rotated and is read straight from the caller's tensor.
 //
 // Design (one workgroup = 8 waves = 256 query rows of one head and one sequence):
 //  * Scores are formed transposed, S^T = K~ Q~^T: a lane owns one query column and 16 keys per
 //    32x32 block, so the softmax row max and row sum are in-lane plus one exchange between the
 //    two 32-lane halves (v_permlane32_swap).
-//  * P^T leaves the score accumulator already in the B-operand layout of the PV product; the V^T
-//    tile in LDS stores keys in the matching order (within each 16 keys: 0-3, 8-11, 4-7, 12-15).
-//  * Three LDS tile buffers: tile j+2 is written while tiles j (PV) and j+1 (scores) are read,
-//    so one barrier per tile suffices; tile j+3 is fetched into registers meanwhile.
-//  * The score product of tile j+1 is issued before the softmax of tile j, so the MFMA pipe works
-//    while the VALU computes exponentials.
+//  * Tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4 (no registers, no VALU) into
+//    four LDS buffers; the copy of tile j+3 is in flight while tile j is consumed, one barrier per
+//    tile.  16-byte chunks are XOR-swizzled by row so that every LDS read below is free of bank
+//    conflicts without padding (the DMA writes each 1 KB block linearly).
+//  * The PV product needs V with keys along each lane's operand; ds_read_b64_tr_b16 reads the
+//    row-major V tile transposed, so V needs no staging pass and no VALU transpose.  The key
+//    order inside each 16 keys matches the order in which the score accumulator hands P^T over
+//    as the B operand (keys 4h..4h+3 then 8+4h..8+4h+3 for lane half h).
+//  * The score product of tile j+1 is issued before the softmax of tile j, so the MFMA pipe has
+//    work while the VALU computes exponentials.  The loop is unrolled by the buffer count so all
+//    LDS addresses are a per-lane base plus an immediate.
 //  * Online softmax with a lazily updated running max: the accumulator is rescaled only when a
 //    row max exceeds the stored one by more than 2^8 (exact in any case; the stored max is only
 //    an offset for the exponentials).
+#include <type_traits>
+
 #include "st_internal.h"
 
 namespace st {
@@ -42,20 +49,24 @@ constexpr int D = 128;          // head dimension
 constexpr int BM = 256;         // query rows per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 512;   // 8 waves
-constexpr int KS = 136;         // K tile row stride in LDS (fp16): 272 B, rows start 4 banks apart
-constexpr int VS = 72;          // V^T tile row stride in LDS (bf16): 144 B
-constexpr int KTILE = BN * KS;
-constexpr int VTILE = D * VS;
-constexpr int NBUF = 3;
+constexpr int NBUF = 4;
+constexpr int TILE_BYTES = BN * D * 2;           // 16 KB, one K~ or V tile
+constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K tiles first, then V tiles
+constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
 constexpr float LAZY_LOG2 = 8.0f;  // rescale when the max grows by more than this (log2 units)
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(1))) const void gptr_t;
 
 struct AttnParams {
     const uint16_t* q;
-    const uint16_t* k;     // FUSED: K [N][heads][D] bf16; staged: K~ tiles, fp16
-    const uint16_t* v;     // FUSED: V [N][heads][D] bf16; staged: V^T tiles, bf16
+    const uint16_t* k;     // staged: K~ tiles (fp16); FUSED: K [N][heads][D] bf16
+    const uint16_t* v;     // V [N][heads][D] bf16
     uint16_t* out;
     const float2* table;
     RopeGeom g;
@@ -70,9 +81,7 @@ struct AttnParams {
 
 struct PrepParams {
     const uint16_t* k;
-    const uint16_t* v;
     uint16_t* kt;          // [heads][n_segs][k_tiles][BN][D] fp16
-    uint16_t* vt;          // [heads][n_segs][k_tiles][D][BN] bf16, keys permuted within 16
     const float2* table;
     RopeGeom g;
     int heads;
@@ -82,7 +91,6 @@ struct PrepParams {
 };
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint2 ld8(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     f16x2_t v = {(_Float16)lo, (_Float16)hi};
@@ -103,18 +111,10 @@ __device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, 
     return make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }
 
-__device__ __forceinline__ uint32_t half16(uint2 v, int e) {
-    uint32_t w = (e < 2) ? v.x : v.y;
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
+// Swizzles: physical 16-byte chunk of logical chunk c in row r of a 256-byte tile row.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
 
-// Position of key 4*grp (a group of 4 consecutive keys) inside a V^T row of 64 keys.
-__device__ __forceinline__ int vt_pos(int grp) {
-    const int sb = grp & 3;
-    return 16 * (grp >> 2) + ((sb & 1) << 3) + ((sb >> 1) << 2);
-}
-
-// Sum over the two 32-lane halves (lane i and i ^ 32) of a wave.
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -124,10 +124,16 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte) {
+    __builtin_amdgcn_global_load_lds((gptr_t*)src, (lds_u8*)(uintptr_t)lds_byte, 16, 0, 0);
+}
+
+template <int B> using Buf = std::integral_constant<int, B>;
+
 template <bool FUSED>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[NBUF][KTILE];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[NBUF][VTILE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
     const int logical = xcd_remap(blockIdx.x, p.total_wg);
     const int qt = logical % p.q_tiles;
@@ -141,85 +147,76 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const RopeGeom& g = p.g;
 
-    // ---- tile copy: global -> registers (load_tile) -> LDS (store_tile) -------------------------
-    uint4 st0, st1, st2, st3;      // staged tile data (meaning depends on the mode)
-    // FUSED geometry: K chunk kc of rows kr0, kr0+32; V channels 4vd.. of keys 4vg..
-    const int kc = tid & 15;
-    const int kr0 = tid >> 4;
-    const int vd = tid & 31;
-    const int vg = tid >> 5;
-    const uint16_t* __restrict__ kbase = p.k + (FUSED ? (long long)head * D : 0);
-    const uint16_t* __restrict__ vbase = p.v + (FUSED ? (long long)head * D : 0);
-    const long long tile0 = ((long long)head * p.n_segs + seg) * ntiles;
-
-    auto load_tile = [&](int j) {
-        if constexpr (FUSED) {
-            int kl0 = j * BN + kr0, kl1 = kl0 + 32;
-            st0 = kl0 < seg_len ? ld16(kbase + (seg_base + kl0) * row_stride + 8 * kc) : make_uint4(0, 0, 0, 0);
-            st1 = kl1 < seg_len ? ld16(kbase + (seg_base + kl1) * row_stride + 8 * kc) : make_uint4(0, 0, 0, 0);
-            uint2 vr[4];
+    // ---- tile copies ------------------------------------------------------------------------
+    // Wave w, copy i in {0,1}: rows r = 8w + 4i + lane/16, physical chunk lane%16 of that row.
+    const int dr0 = 8 * wave + (lane >> 4);
+    const int pc = lane & 15;
+    const uint16_t* vhead = p.v + (long long)head * D;
+    const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
+    int k_src_off[2];   // staged: element offset inside a K~ tile
+    int v_chunk[2];     // element offset of the lane's logical chunk inside a V row
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                int kl = j * BN + 4 * vg + r;
-                vr[r] = kl < seg_len ? ld8(vbase + (seg_base + kl) * row_stride + 4 * vd) : make_uint2(0, 0);
-            }
-            st2 = make_uint4(vr[0].x, vr[0].y, vr[1].x, vr[1].y);
-            st3 = make_uint4(vr[2].x, vr[2].y, vr[3].x, vr[3].y);
+    for (int i = 0; i < 2; ++i) {
+        const int r = dr0 + 4 * i;
+        k_src_off[i] = r * D + 8 * (pc ^ k_swz(r));
+        v_chunk[i] = 8 * (pc ^ v_swz(r));
+    }
+    // FUSED K copy through registers: thread owns chunks c = tid & 15 of rows tid>>4 and +32.
+    const int fkc = tid & 15;
+    const int fkr = tid >> 4;
+    uint4 fk0 = make_uint4(0, 0, 0, 0), fk1 = make_uint4(0, 0, 0, 0);
+
+    auto issue_tile = [&](int j, int buf) {
+        const uint32_t kl = lds0 + buf * TILE_BYTES + (8 * wave) * 256;
+        const uint32_t vl = lds0 + V_LDS_BASE + buf * TILE_BYTES + (8 * wave) * 256;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            int key = j * BN + dr0 + 4 * i;
+            key = key < seg_len ? key : seg_len - 1;   // rows past the end repeat the last row
+            dma16(vhead + (seg_base + key) * row_stride + v_chunk[i], vl + i * 1024);
+        }
+        if constexpr (!FUSED) {
+            const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) dma16(kt + k_src_off[i], kl + i * 1024);
         } else {
-            const uint16_t* kt = kbase + (tile0 + j) * (BN * D);
-            const uint16_t* vt = vbase + (tile0 + j) * (BN * D);
-            st0 = ld16(kt + 8 * tid);
-            st1 = ld16(kt + 8 * (tid + NTHREADS));
-            st2 = ld16(vt + 8 * tid);
-            st3 = ld16(vt + 8 * (tid + NTHREADS));
+            const uint16_t* kh = p.k + (long long)head * D;
+            const int k0 = j * BN + fkr, k1 = k0 + 32;
+            fk0 = k0 < seg_len ? ld16(kh + (seg_base + k0) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
+            fk1 = k1 < seg_len ? ld16(kh + (seg_base + k1) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_tile = [&](int j, int buf) {
-        uint16_t* lk = lds_k[buf];
-        uint16_t* lv = lds_v[buf];
+    // FUSED only: rotate the registers fetched by issue_tile(j, buf) and write them to LDS.
+    auto finish_tile = [&](int j, int buf) {
         if constexpr (FUSED) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const int r = kr0 + 32 * i;
+                const int r = fkr + 32 * i;
                 const int n = seg_base + j * BN + r;
                 int t = 0, h = 0, w = 0;
                 const bool text = n >= g.Nv;
                 if (!text) decode_pos(n, g, t, h, w);
-                uint4 rot = rope_chunk_f16(i == 0 ? st0 : st1, kc, t, h, w, text, g, p.table);
-                *reinterpret_cast<uint4*>(&lk[r * KS + 8 * kc]) = rot;
-            }
-            uint2 vr[4] = {make_uint2(st2.x, st2.y), make_uint2(st2.z, st2.w),
-                           make_uint2(st3.x, st3.y), make_uint2(st3.z, st3.w)};
-            const int pos = vt_pos(vg);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                uint32_t w0 = half16(vr[0], e) | (half16(vr[1], e) << 16);
-                uint32_t w1 = half16(vr[2], e) | (half16(vr[3], e) << 16);
-                *reinterpret_cast<uint2*>(&lv[(4 * vd + e) * VS + pos]) = make_uint2(w0, w1);
+                uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, text, g, p.table);
+                const uint32_t a = lds0 + buf * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
+                const u32x4_t rv = {rot.x, rot.y, rot.z, rot.w};
+                *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)a = rv;
             }
         } else {
             (void)j;
-            const int c0 = tid, c1 = tid + NTHREADS;
-            *reinterpret_cast<uint4*>(&lk[(c0 >> 4) * KS + 8 * (c0 & 15)]) = st0;
-            *reinterpret_cast<uint4*>(&lk[(c1 >> 4) * KS + 8 * (c1 & 15)]) = st1;
-            *reinterpret_cast<uint4*>(&lv[(c0 >> 3) * VS + 8 * (c0 & 7)]) = st2;
-            *reinterpret_cast<uint4*>(&lv[(c1 >> 3) * VS + 8 * (c1 & 7)]) = st3;
+            (void)buf;
         }
     };
 
-    // ---- prologue ---------------------------------------------------------------------------------
-    load_tile(0);
-    store_tile(0, 0);
-    if (ntiles > 1) {
-        load_tile(1);
-        store_tile(1, 1);
-    }
-    if (ntiles > 2) load_tile(2);
+    // ---- prologue -----------------------------------------------------------------------------
+    issue_tile(0, 0);
+    finish_tile(0, 0);
+    if (ntiles > 1) { issue_tile(1, 1); finish_tile(1, 1); }
+    if (ntiles > 2) { issue_tile(2, 2); finish_tile(2, 2); }
 
     const int q_local = qt * BM + wave * 32 + l32;
     const bool q_valid = q_local < seg_len;
@@ -237,20 +234,45 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             qreg[ks] = __builtin_bit_cast(f16x8_t, rope_chunk_f16(raw, c, t, h, w, text, g, p.table));
         }
     }
-    __syncthreads();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 
-    auto qk = [&](int buf, f32x16_t (&s)[2]) {
-        const uint16_t* lk = lds_k[buf];
+    // ---- per-lane LDS read addresses -------------------------------------------------------------
+    // K operand of the score product: row l32 (+32 for the second block), logical chunk 2ks + hh.
+    uint32_t k_rd[4];
+    {
+        const int x = l32 & 7;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int t = 0; t < 4; ++t)
+            k_rd[t] = lds0 + l32 * 256 + 16 * (((2 * t) ^ (x & 6)) + ((hh ^ x) & 1));
+    }
+    // V operand of the PV product, read transposed: lane (i = lane%16, g = lane/16) points at row
+    // 4*(g/2) + i/4 (+ 16 per key chunk, + 8 for the upper half), channels 16*(g%2) + 4*(i%4).
+    uint32_t v_rd[2];
+    {
+        const int i = lane & 15, gq = lane >> 4;
+        const int row = 4 * (gq >> 1) + (i >> 2);
+        const int u = 2 * (gq & 1) + ((i & 3) >> 1);
+        const int ph = u ^ v_swz(row);
+        v_rd[0] = lds0 + V_LDS_BASE + row * 256 + 16 * ph + 8 * (i & 1);
+        v_rd[1] = lds0 + V_LDS_BASE + row * 256 + 16 * (ph ^ 4) + 8 * (i & 1);
+    }
+
+    auto qk = [&](auto bufc, f32x16_t (&s)[2]) {
+        constexpr int b = decltype(bufc)::value;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[mb][i] = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                f16x8_t a = *reinterpret_cast<const f16x8_t*>(&lk[(32 * mb + l32) * KS + 16 * ks + 8 * hh]);
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qreg[ks], s[mb], 0, 0, 0);
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const uint32_t a = k_rd[ks & 3] + b * TILE_BYTES + (ks >> 2) * 128 + mb * 32 * 256;
+                f16x8_t op = *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op, qreg[ks], s[mb], 0, 0, 0);
             }
-        }
     };
 
     f32x16_t oacc[4];
@@ -266,10 +288,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
     // One tile step: softmax and PV of tile j (scores in sc) while the scores of tile j+1 are
-    // formed into sn.
-    auto step = [&](int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-        const int b = j % NBUF;
-        if (j + 1 < ntiles) qk((j + 1) % NBUF, sn);
+    // formed into sn and tile j+3 is copied into LDS.
+    auto step = [&](auto bufc, int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+        constexpr int b = decltype(bufc)::value;
+        constexpr int b1 = (b + 1) % NBUF;
+        constexpr int b3 = (b + 3) % NBUF;
+        const bool issue = j + 3 < ntiles;
+        if (issue) issue_tile(j + 3, b3);
+        if (j + 1 < ntiles) qk(Buf<b1>{}, sn);
 
         if (ragged && j == ntiles - 1) {
 #pragma unroll
@@ -280,11 +306,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                     if (key >= seg_len) sc[mb][i] = -INFINITY;
                 }
         }
-        float mx = fmaxf(sc[0][0], sc[0][1]);
+        float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
 #pragma unroll
-        for (int i = 2; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[0][i], sc[0][i + 1]));
+        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[0][i]), sc[0][i + 1]);
+        mx = fmaxf(mx, sc[0][15]);
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sc[1][i], sc[1][i + 1]));
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[1][i]), sc[1][i + 1]);
         mx = xhalf_max(mx);
         const bool grow = mx > m_run + lazy_raw;
         if (__any(grow)) {
@@ -313,27 +340,42 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             }
             pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
         }
-        const uint16_t* lv = lds_v[b];
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&lv[(32 * db + l32) * VS + 16 * c + 8 * hh]);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c], oacc[db], 0, 0, 0);
+            for (int db = 0; db < 4; ++db) {
+                const uint32_t a = v_rd[db & 1] + b * TILE_BYTES + (db >> 1) * 128 + c * 16 * 256;
+                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
+                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 8 * 256));
+                const bf16x8_t op = __builtin_bit_cast(
+                    bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[c], oacc[db], 0, 0, 0);
             }
-        if (j + 2 < ntiles) store_tile(j + 2, (j + 2) % NBUF);
-        if (j + 3 < ntiles) load_tile(j + 3);
-        __syncthreads();
+        if constexpr (FUSED) {
+            if (issue) finish_tile(j + 3, b3);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        } else {
+            // Tile j+2 (issued one step earlier) must have landed; tile j+3 may stay in flight.
+            if (issue) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
     };
 
     f32x16_t sa[2], sb[2];
-    qk(0, sa);
-    int j = 0;
-    for (; j + 1 < ntiles; j += 2) {
-        step(j, sa, sb);
-        step(j + 1, sb, sa);
+    qk(Buf<0>{}, sa);
+    for (int j = 0; j < ntiles; j += 4) {
+        step(Buf<0>{}, j, sa, sb);
+        if (j + 1 >= ntiles) break;
+        step(Buf<1>{}, j + 1, sb, sa);
+        if (j + 2 >= ntiles) break;
+        step(Buf<2>{}, j + 2, sa, sb);
+        if (j + 3 >= ntiles) break;
+        step(Buf<3>{}, j + 3, sb, sa);
     }
-    if (j < ntiles) step(j, sa, sb);
 
     // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
     const float inv = 1.0f / xhalf_sum(l_run);
@@ -352,50 +394,29 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     }
 }
 
-// Preparation for the staged mode: one workgroup per (head, segment, key tile) rotates the tile's
-// 64 K rows into fp16 and writes the V tile transposed (keys permuted within each 16 as the PV
-// operand expects).  Rows past the segment are written as zeros.
-__global__ void __launch_bounds__(256) kv_prep_kernel(PrepParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lv[BN * KS];
+// Staging for the default mode: one workgroup per (head, segment, key tile) rotates the tile's
+// 64 K rows into fp16.  Rows past the segment are written as zeros.
+__global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
     const int tile = blockIdx.x;
     const int kt = tile % p.k_tiles;
     const int rest = tile / p.k_tiles;
     const int seg = rest % p.n_segs;
     const int head = rest / p.n_segs;
     const long long row_stride = (long long)p.heads * D;
-    const int tid = threadIdx.x;
     const RopeGeom& g = p.g;
-    uint16_t* kt_out = p.kt + (long long)tile * (BN * D);
-    uint16_t* vt_out = p.vt + (long long)tile * (BN * D);
+    uint16_t* out = p.kt + (long long)tile * (BN * D);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int id = tid + 256 * i;
+        const int id = threadIdx.x + 256 * i;
         const int r = id >> 4, c = id & 15;
         const int kl = kt * BN + r;
         const bool valid = kl < p.seg_len;
         const int n = seg * p.seg_len + (valid ? kl : 0);
-        const long long off = n * row_stride + (long long)head * D + 8 * c;
-        uint4 kraw = valid ? ld16(p.k + off) : make_uint4(0, 0, 0, 0);
-        uint4 vraw = valid ? ld16(p.v + off) : make_uint4(0, 0, 0, 0);
+        uint4 raw = valid ? ld16(p.k + n * row_stride + (long long)head * D + 8 * c) : make_uint4(0, 0, 0, 0);
         int t = 0, h = 0, w = 0;
         const bool text = n >= g.Nv;
         if (!text) decode_pos(n, g, t, h, w);
-        *reinterpret_cast<uint4*>(kt_out + r * D + 8 * c) = rope_chunk_f16(kraw, c, t, h, w, text, g, p.table);
-        *reinterpret_cast<uint4*>(&lv[r * KS + 8 * c]) = vraw;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int id = tid + 256 * i;
-        const int d = id >> 3, c8 = id & 7;
-        const int k0 = 16 * (c8 >> 1) + 4 * (c8 & 1);
-        uint32_t wd[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ka = k0 + (e < 2 ? 2 * e : 8 + 2 * (e - 2));
-            wd[e] = (uint32_t)lv[ka * KS + d] | ((uint32_t)lv[(ka + 1) * KS + d] << 16);
-        }
-        *reinterpret_cast<uint4*>(vt_out + d * BN + 8 * c8) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+        *reinterpret_cast<uint4*>(out + r * D + 8 * c) = rope_chunk_f16(raw, c, t, h, w, text, g, p.table);
     }
 }
 
@@ -418,6 +439,12 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     return p;
 }
 
+template <bool FUSED>
+hipError_t launch(const AttnParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(attn_fwd_kernel<FUSED>, dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 size_t attn_stage_elems(int heads, int seg_len, int n_segs) {
@@ -425,14 +452,11 @@ size_t attn_stage_elems(int heads, int seg_len, int n_segs) {
     return (size_t)heads * n_segs * k_tiles * BN * D;
 }
 
-hipError_t launch_kv_prep(const uint16_t* k, const uint16_t* v, uint16_t* kt, uint16_t* vt,
-                          const float2* table, const RopeGeom& g, int heads, int seg_len,
-                          int n_segs, hipStream_t stream) {
+hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
+                         int heads, int seg_len, int n_segs, hipStream_t stream) {
     PrepParams p;
     p.k = k;
-    p.v = v;
     p.kt = kt;
-    p.vt = vt;
     p.table = table;
     p.g = g;
     p.heads = heads;
@@ -440,24 +464,20 @@ hipError_t launch_kv_prep(const uint16_t* k, const uint16_t* v, uint16_t* kt, ui
     p.n_segs = n_segs;
     p.k_tiles = (seg_len + BN - 1) / BN;
     const int blocks = heads * n_segs * p.k_tiles;
-    hipLaunchKernelGGL(kv_prep_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_prep_kernel, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* vt,
+hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, const float2* table, const RopeGeom& g,
                                    int heads, int seg_len, int n_segs, hipStream_t stream) {
-    AttnParams p = make_params(q, kt, vt, out, table, g, heads, seg_len, n_segs);
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
-    return hipGetLastError();
+    return launch<false>(make_params(q, kt, v, out, table, g, heads, seg_len, n_segs), stream);
 }
 
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* out, const float2* table, const RopeGeom& g,
                                   int heads, int seg_len, int n_segs, hipStream_t stream) {
-    AttnParams p = make_params(q, k, v, out, table, g, heads, seg_len, n_segs);
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
-    return hipGetLastError();
+    return launch<true>(make_params(q, k, v, out, table, g, heads, seg_len, n_segs), stream);
 }
 
 }  // namespace st

@@ -112,10 +112,10 @@ st_status hip_fail(hipError_t e) {
     return ST_ERR_HIP;
 }
 
-// Byte layout of the bf16 staged workspace: [table][K~ tiles][V^T tiles], each 256-aligned.
+// Byte layout of the bf16 staged workspace: [table][K~ tiles], each 256-aligned.
 struct StageLayout {
     size_t table_bytes;
-    size_t tiles_bytes;   // one of the two tile arrays
+    size_t tiles_bytes;
     size_t total;
 };
 
@@ -123,7 +123,7 @@ StageLayout stage_layout(int T, int H, int W, int heads, int seg_len, int n_segs
     StageLayout L;
     L.table_bytes = table_bytes_for(T, H, W, split);
     L.tiles_bytes = align_up(st::attn_stage_elems(heads, seg_len, n_segs) * 2, kWsAlign);
-    L.total = L.table_bytes + 2 * L.tiles_bytes;
+    L.total = L.table_bytes + L.tiles_bytes;
     return L;
 }
 
@@ -174,12 +174,12 @@ size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split
     return st_rope3d_table_bytes(T, H, W, rope_split);
 }
 
-st_status st_attn3d_stage(const void* k, const void* v, int T, int H, int W, int n_text, int heads,
-                          int d, const int rope_split[3], float theta, st_dtype dtype,
-                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int heads, int d,
+                          const int rope_split[3], float theta, st_dtype dtype, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
     long long n = 0;
-    // q is not read by this step; pass k in its place for the shared checks.
-    st_status s = check_attn(k, k, v, workspace, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    // Only k is read by this step; it stands in for q and v in the shared checks.
+    st_status s = check_attn(k, k, k, workspace, T, H, W, n_text, heads, d, rope_split, dtype, &n);
     if (s == ST_ERR_ALIAS) s = ST_OK;  // workspace aliasing is checked below with its true size
     if (s != ST_OK) return s;
     if (dtype != ST_BF16) return ST_ERR_UNSUPPORTED;
@@ -187,38 +187,36 @@ st_status st_attn3d_stage(const void* k, const void* v, int T, int H, int W, int
     if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
     StageLayout L = stage_layout(T, H, W, heads, (int)n, 1, rope_split);
     if (ws_bytes < L.total) return ST_ERR_WORKSPACE;
-    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, k, v, nullptr, nullptr))
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, k, nullptr, nullptr, nullptr))
         return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
     char* ws = (char*)workspace;
     float2* table = (float2*)ws;
     hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
     if (e != hipSuccess) return hip_fail(e);
-    e = st::launch_kv_prep((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)(ws + L.table_bytes),
-                           (uint16_t*)(ws + L.table_bytes + L.tiles_bytes), table, g, heads, (int)n, 1,
-                           stream);
+    e = st::launch_k_prep((const uint16_t*)k, (uint16_t*)(ws + L.table_bytes), table, g, heads, (int)n,
+                          1, stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
-st_status st_attn3d_attend(const void* q, int T, int H, int W, int n_text, int heads, int d,
-                           const int rope_split[3], st_dtype dtype, const void* workspace,
+st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, int n_text, int heads,
+                           int d, const int rope_split[3], st_dtype dtype, const void* workspace,
                            size_t ws_bytes, void* out, hipStream_t stream) {
     long long n = 0;
     if (!workspace) return ST_ERR_NULL;
-    st_status s = check_attn(q, q, q, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    st_status s = check_attn(q, q, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
     if (dtype != ST_BF16) return ST_ERR_UNSUPPORTED;
     if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
     StageLayout L = stage_layout(T, H, W, heads, (int)n, 1, rope_split);
     if (ws_bytes < L.total) return ST_ERR_WORKSPACE;
-    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, q, out, nullptr, nullptr))
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, q, v, out, nullptr))
         return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
     const char* ws = (const char*)workspace;
-    hipError_t e = st::launch_attn_bf16_staged(
-        (const uint16_t*)q, (const uint16_t*)(ws + L.table_bytes),
-        (const uint16_t*)(ws + L.table_bytes + L.tiles_bytes), (uint16_t*)out, (const float2*)ws, g,
-        heads, (int)n, 1, stream);
+    hipError_t e = st::launch_attn_bf16_staged((const uint16_t*)q, (const uint16_t*)(ws + L.table_bytes),
+                                               (const uint16_t*)v, (uint16_t*)out, (const float2*)ws, g,
+                                               heads, (int)n, 1, stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -237,11 +235,11 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int 
     if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * elem_size(dtype), q, k, v, out))
         return ST_ERR_ALIAS;
     if (dtype == ST_BF16) {
-        s = st_attn3d_stage(k, v, T, H, W, n_text, heads, d, rope_split, theta, dtype, workspace,
+        s = st_attn3d_stage(k, T, H, W, n_text, heads, d, rope_split, theta, dtype, workspace,
                             ws_bytes, stream);
         if (s != ST_OK) return s;
-        return st_attn3d_attend(q, T, H, W, n_text, heads, d, rope_split, dtype, workspace, ws_bytes,
-                                out, stream);
+        return st_attn3d_attend(q, v, T, H, W, n_text, heads, d, rope_split, dtype, workspace,
+                                ws_bytes, out, stream);
     }
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
     float2* table = (float2*)workspace;
@@ -315,12 +313,11 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
     if (dtype == ST_BF16) {
         StageLayout L = stage_layout(T, H, W, heads, S, T, rope_split);
         uint16_t* kt = (uint16_t*)(ws + L.table_bytes);
-        uint16_t* vt = (uint16_t*)(ws + L.table_bytes + L.tiles_bytes);
         uint16_t* o_s = (uint16_t*)(ws + L.total);
-        e = st::launch_kv_prep((const uint16_t*)k, (const uint16_t*)v, kt, vt, table, g, heads, S, T,
-                               stream);
+        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, S, T, stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, vt, o_s, table, g, heads, S, T, stream);
+        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, o_s, table, g, heads,
+                                        S, T, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, o_s, (uint16_t*)out,
                                           table, g, heads, stream);

@@ -101,14 +101,13 @@ hipError_t launch_rope_apply_f32(const float* x, float* y, const RopeGeom& g, in
 // [s * seg_len, (s + 1) * seg_len) for s < n_segs: one segment of N rows for full attention,
 // T segments of H*W rows for the factorised spatial stage.
 //
-// Staged mode: launch_kv_prep rotates K into fp16 tiles `kt` and transposes V into tiles `vt`
-// (attn_stage_elems(...) uint16 elements each), then launch_attn_bf16_staged reads them.
-// Fused mode: launch_attn_bf16_fused reads K and V directly and rotates K on every tile load.
+// Staged mode: launch_k_prep rotates K into fp16 tiles `kt` (attn_stage_elems(...) uint16
+// elements), then launch_attn_bf16_staged reads them together with V.
+// Fused mode: launch_attn_bf16_fused reads K directly and rotates it on every tile load.
 size_t attn_stage_elems(int heads, int seg_len, int n_segs);
-hipError_t launch_kv_prep(const uint16_t* k, const uint16_t* v, uint16_t* kt, uint16_t* vt,
-                          const float2* table, const RopeGeom& g, int heads, int seg_len,
-                          int n_segs, hipStream_t stream);
-hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* vt,
+hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
+                         int heads, int seg_len, int n_segs, hipStream_t stream);
+hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, const float2* table, const RopeGeom& g,
                                    int heads, int seg_len, int n_segs, hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -86,9 +86,10 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  * ("full 3D attention", first page, self-test answer 2 and "How attention sees time").
  *
  * ST_BF16 runs in two steps, both on `stream`:
- *   stage:  the angle table, the rotated K rows as fp16 tiles and the V rows transposed into
- *           tiles, all written into the caller's workspace (one pass over K and V);
- *   attend: the attention kernel; it rotates Q itself and streams the staged K/V tiles.
+ *   stage:  the angle table and the rotated K rows as fp16 tiles of 64 keys, written into the
+ *           caller's workspace (one pass over K);
+ *   attend: the attention kernel; it rotates Q itself and streams the staged K tiles and the
+ *           caller's V.
  * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
  * fp16 for the score product, so every rotated q/k entry must stay below 65504 in magnitude
  * (inputs with |x| < 2^15 are always safe); softmax weights multiply V in bf16.
@@ -96,7 +97,8 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  * ------------------------------------------------------------------------------------------- */
 
 /* Workspace bytes st_attn3d_fwd (and stage/attend) need; 0 if the arguments are invalid.
- * ST_BF16: table + 2 x heads x ceil(N/64) x 64 x d x 2 bytes; ST_F32: table. */
+ * ST_BF16: table + heads x ceil(N/64) x 64 x d x 2 bytes (256-byte aligned parts); ST_F32:
+ * table. */
 size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
                                  const int rope_split[3], st_dtype dtype);
 
@@ -107,25 +109,25 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v,
                         const int rope_split[3], float theta, st_dtype dtype,
                         void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
-/* First step of the ST_BF16 path: fill `workspace` from k and v.  ST_F32 is not served here
+/* First step of the ST_BF16 path: fill `workspace` from k.  ST_F32 is not served here
  * (ST_ERR_UNSUPPORTED). */
-st_status st_attn3d_stage(const void* k, const void* v,
-                          int T, int H, int W, int n_text, int heads, int d,
+st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int heads, int d,
                           const int rope_split[3], float theta, st_dtype dtype,
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
-/* Second step of the ST_BF16 path: attention of q against a workspace that st_attn3d_stage
- * filled for the same grid, n_text, heads, d and rope_split (read only).  One kernel launch. */
-st_status st_attn3d_attend(const void* q, int T, int H, int W, int n_text, int heads, int d,
-                           const int rope_split[3], st_dtype dtype,
+/* Second step of the ST_BF16 path: attention of q against the K tiles st_attn3d_stage wrote
+ * for the same grid, n_text, heads, d and rope_split (read only), with values v.  One kernel
+ * launch. */
+st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, int n_text,
+                           int heads, int d, const int rope_split[3], st_dtype dtype,
                            const void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* Workspace bytes of st_attn3d_fwd_fused: the angle table only. */
 size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split[3]);
 
 /* The same result with RoPE fused into the attention kernel's tile loads: every K tile is
- * rotated (position decoded from its flat row index) and every V tile transposed while it is
- * copied into LDS, with no staging pass.  Two launches (table, attention).  ST_F32 runs the
+ * rotated (position decoded from its flat row index) while it is copied into LDS, with no
+ * staging pass.  Two launches (table, attention).  ST_F32 runs the
  * fp32 kernel as st_attn3d_fwd does. */
 st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
                               int T, int H, int W, int n_text, int heads, int d,
@@ -139,7 +141,7 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
  * (n_text is 0 by construction: N = T*H*W).
  * ------------------------------------------------------------------------------------------- */
 
-/* Workspace bytes: the angle table, for ST_BF16 the staged K/V tiles of the per-frame sequences
+/* Workspace bytes: the angle table, for ST_BF16 the staged K tiles of the per-frame sequences
  * (as for st_attn3d_fwd), and the stage-1 output [N][heads][d] of `dtype`. */
 size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
                                           const int rope_split[3], st_dtype dtype);

@@ -78,12 +78,12 @@ def test_table_bytes(lib):
 
 
 def test_attn3d_workspace_bytes(lib):
-    # bf16: table + rotated-K tiles + transposed-V tiles, each 64 keys x 128 channels x 2 bytes
+    # bf16: table + rotated-K tiles of 64 keys x 128 channels x 2 bytes
     for (t, h, w), n_text, heads in [((21, 30, 52), 0, 12), ((33, 45, 80), 256, 24), ((1, 1, 1), 0, 1)]:
         n = t * h * w + n_text
         tb = lib.st_rope3d_table_bytes(t, h, w, sp(44, 42, 42))
         tiles = ((heads * ((n + 63) // 64) * 64 * 128 * 2) + 255) // 256 * 256
-        assert lib.st_attn3d_workspace_bytes(t, h, w, n_text, heads, 128, sp(44, 42, 42), 0) == tb + 2 * tiles
+        assert lib.st_attn3d_workspace_bytes(t, h, w, n_text, heads, 128, sp(44, 42, 42), 0) == tb + tiles
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, 0, 2, 64, sp(20, 22, 22), 0) == 0   # bf16 d != 128
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, 0, 0, 128, sp(44, 42, 42), 0) == 0
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, -1, 2, 128, sp(44, 42, 42), 0) == 0
@@ -95,7 +95,7 @@ def test_factorized_workspace_bytes(lib):
     n = 21 * 30 * 52
     tiles = (12 * 21 * ((1560 + 63) // 64) * 64 * 128 * 2 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 0) == \
-        tb + 2 * tiles + (n * 12 * 128 * 2 + 255) // 256 * 256
+        tb + tiles + (n * 12 * 128 * 2 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 1) == \
         tb + (n * 12 * 128 * 4 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 0, 128, sp(44, 42, 42), 0) == 0
@@ -146,16 +146,16 @@ def test_stage_attend_fused_reject_invalid_arguments(lib):
     wsb = lib.st_attn3d_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0)
 
     def stage(**kw):
-        a = dict(k=K, v=V, T=3, d=128, split=(44, 42, 42), theta=1e4, dtype=0, ws=WS, ws_bytes=wsb)
+        a = dict(k=K, T=3, d=128, split=(44, 42, 42), theta=1e4, dtype=0, ws=WS, ws_bytes=wsb)
         a.update(kw)
-        return lib.st_attn3d_stage(a["k"], a["v"], a["T"], 4, 6, 0, 2, a["d"], sp(*a["split"]),
+        return lib.st_attn3d_stage(a["k"], a["T"], 4, 6, 0, 2, a["d"], sp(*a["split"]),
                                    a["theta"], a["dtype"], a["ws"], a["ws_bytes"], None)
 
     def attend(**kw):
-        a = dict(q=Q, dtype=0, ws=WS, ws_bytes=wsb, out=OUT)
+        a = dict(q=Q, v=V, dtype=0, ws=WS, ws_bytes=wsb, out=OUT)
         a.update(kw)
-        return lib.st_attn3d_attend(a["q"], 3, 4, 6, 0, 2, 128, sp(44, 42, 42), a["dtype"], a["ws"],
-                                    a["ws_bytes"], a["out"], None)
+        return lib.st_attn3d_attend(a["q"], a["v"], 3, 4, 6, 0, 2, 128, sp(44, 42, 42), a["dtype"],
+                                    a["ws"], a["ws_bytes"], a["out"], None)
 
     def fused(**kw):
         a = dict(q=Q, dtype=0, ws=WS, ws_bytes=4096, out=OUT, theta=1e4)
@@ -173,11 +173,14 @@ def test_stage_attend_fused_reject_invalid_arguments(lib):
     assert stage(ws=WS + 128) == ST_ERR_ALIGN
     assert stage(ws=K) == ST_ERR_ALIAS
     assert attend(q=None) == ST_ERR_NULL
+    assert attend(v=None) == ST_ERR_NULL
     assert attend(ws=None) == ST_ERR_NULL
     assert attend(dtype=1) == ST_ERR_UNSUPPORTED
     assert attend(ws_bytes=1024) == ST_ERR_WORKSPACE
     assert attend(out=Q) == ST_ERR_ALIAS
+    assert attend(out=V) == ST_ERR_ALIAS
     assert attend(ws=OUT) == ST_ERR_ALIAS
+    assert attend(ws=V) == ST_ERR_ALIAS
     assert fused(q=None) == ST_ERR_NULL
     assert fused(ws=None) == ST_ERR_NULL
     assert fused(ws_bytes=8) == ST_ERR_WORKSPACE

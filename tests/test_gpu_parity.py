@@ -153,8 +153,8 @@ def test_stage_attend_matches_fwd_bitwise():
     x = make_qkv(495, heads, 128, 400, "bf16")
     q, k, v = to_device(x)
     a = fa.attn3d(q, k, v, grid)
-    ws = fa.attn3d_stage(k, v, grid)
-    b = fa.attn3d_attend(q, grid, ws)
+    ws = fa.attn3d_stage(k, grid)
+    b = fa.attn3d_attend(q, v, grid, ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
