@@ -49,9 +49,10 @@ constexpr int D = 128;          // head dimension
 constexpr int BM = 256;         // query rows per workgroup
 constexpr int BN = 64;          // keys per tile
 constexpr int NTHREADS = 512;   // 8 waves
-constexpr int NBUF = 4;
 constexpr int TILE_BYTES = BN * D * 2;           // 16 KB, one K~ or V tile
-constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K tiles first, then V tiles
+constexpr int NBUF = 4;                          // tile j lives in K and V slot j % NBUF
+constexpr int PREF = 3;                          // step j fetches tile j + PREF
+constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
 constexpr float LAZY_LOG2 = 8.0f;  // rescale when the max grows by more than this (log2 units)
 
@@ -111,9 +112,13 @@ __device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, 
     return make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }
 
-// Swizzles: physical 16-byte chunk of logical chunk c in row r of a 256-byte tile row.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
-__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
+// Swizzles: logical 16-byte chunk c of tile row r (256 bytes) sits at physical chunk c ^ swz(r).
+// gfx950 LDS serves 256 bytes per clock from 64 banks: 16 lanes of a 16-byte read or 32 lanes
+// of an 8-byte read at a time.  The K operand read has 16 lanes on 16 consecutive rows at one
+// logical chunk; the transposed V read has 32 lanes on 4 consecutive rows x 4 logical chunks
+// (4db .. 4db+3).  With these swizzles each such group touches 16 different physical chunks.
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 2; }
 
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -124,11 +129,23 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte) {
-    __builtin_amdgcn_global_load_lds((gptr_t*)src, (lds_u8*)(uintptr_t)lds_byte, 16, 0, 0);
+// HBM -> LDS copy of 16 bytes per lane: lane L's bytes from base + voff land at LDS byte address
+// lds + 16 L (global_load_lds_dwordx4, M0 = lds).  Written as inline asm so that the compiler does
+// not treat later LDS reads as waiting on it; the kernel waits for these copies explicitly with
+// s_waitcnt vmcnt before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
 }
 
 template <int B> using Buf = std::integral_constant<int, B>;
+
+// Instruction-class masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002;
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
 
 template <bool FUSED>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
@@ -158,12 +175,12 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const int pc = lane & 15;
     const uint16_t* vhead = p.v + (long long)head * D;
     const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
-    int k_src_off[2];   // staged: element offset inside a K~ tile
-    int v_chunk[2];     // element offset of the lane's logical chunk inside a V row
+    uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
+    int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int r = dr0 + 4 * i;
-        k_src_off[i] = r * D + 8 * (pc ^ k_swz(r));
+        k_src_off[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ k_swz(r)));
         v_chunk[i] = 8 * (pc ^ v_swz(r));
     }
     // FUSED K copy through registers: thread owns chunks c = tid & 15 of rows tid>>4 and +32.
@@ -171,19 +188,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const int fkr = tid >> 4;
     uint4 fk0 = make_uint4(0, 0, 0, 0), fk1 = make_uint4(0, 0, 0, 0);
 
-    auto issue_tile = [&](int j, int buf) {
-        const uint32_t kl = lds0 + buf * TILE_BYTES + (8 * wave) * 256;
-        const uint32_t vl = lds0 + V_LDS_BASE + buf * TILE_BYTES + (8 * wave) * 256;
+    // issue_tile(j, slot): fetch tile j into K and V slot `slot`.
+    auto issue_tile = [&](int j, int slot) {
+        const uint32_t kl = lds0 + slot * TILE_BYTES + (8 * wave) * 256;
+        const uint32_t vl = lds0 + V_LDS_BASE + slot * TILE_BYTES + (8 * wave) * 256;
+        const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
+        const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            int key = j * BN + dr0 + 4 * i;
-            key = key < seg_len ? key : seg_len - 1;   // rows past the end repeat the last row
-            dma16(vhead + (seg_base + key) * row_stride + v_chunk[i], vl + i * 1024);
+            const int r = dr0 + 4 * i;
+            const int re = r < last ? r : last;
+            dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
         }
         if constexpr (!FUSED) {
             const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) dma16(kt + k_src_off[i], kl + i * 1024);
+            for (int i = 0; i < 2; ++i) dma16(kt, k_src_off[i], kl + i * 1024);
         } else {
             const uint16_t* kh = p.k + (long long)head * D;
             const int k0 = j * BN + fkr, k1 = k0 + 32;
@@ -191,8 +211,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             fk1 = k1 < seg_len ? ld16(kh + (seg_base + k1) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
         }
     };
-    // FUSED only: rotate the registers fetched by issue_tile(j, buf) and write them to LDS.
-    auto finish_tile = [&](int j, int buf) {
+    // FUSED only: rotate the K registers fetched by issue_tile(j, slot) and write them to LDS.
+    auto finish_tile = [&](int j, int slot) {
         if constexpr (FUSED) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
@@ -202,21 +222,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                 const bool text = n >= g.Nv;
                 if (!text) decode_pos(n, g, t, h, w);
                 uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, text, g, p.table);
-                const uint32_t a = lds0 + buf * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
+                const uint32_t a = lds0 + slot * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
                 const u32x4_t rv = {rot.x, rot.y, rot.z, rot.w};
                 *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)a = rv;
             }
         } else {
             (void)j;
-            (void)buf;
+            (void)slot;
         }
     };
 
     // ---- prologue -----------------------------------------------------------------------------
-    issue_tile(0, 0);
-    finish_tile(0, 0);
-    if (ntiles > 1) { issue_tile(1, 1); finish_tile(1, 1); }
-    if (ntiles > 2) { issue_tile(2, 2); finish_tile(2, 2); }
+#pragma unroll
+    for (int j = 0; j < PREF; ++j) {
+        issue_tile(min(j, ntiles - 1), j);
+        finish_tile(min(j, ntiles - 1), j);
+    }
 
     const int q_local = qt * BM + wave * 32 + l32;
     const bool q_valid = q_local < seg_len;
@@ -238,41 +259,58 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
-    // ---- per-lane LDS read addresses -------------------------------------------------------------
+    // ---- per-lane LDS read addresses (slot 0; other slots add a multiple of TILE_BYTES) --------
     // K operand of the score product: row l32 (+32 for the second block), logical chunk 2ks + hh.
-    uint32_t k_rd[4];
-    {
-        const int x = l32 & 7;
+    uint32_t k_rd[8];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            k_rd[t] = lds0 + l32 * 256 + 16 * (((2 * t) ^ (x & 6)) + ((hh ^ x) & 1));
-    }
+    for (int ks = 0; ks < 8; ++ks) k_rd[ks] = lds0 + l32 * 256 + 16 * ((2 * ks + hh) ^ k_swz(l32));
     // V operand of the PV product, read transposed: lane (i = lane%16, g = lane/16) points at row
-    // 4*(g/2) + i/4 (+ 16 per key chunk, + 8 for the upper half), channels 16*(g%2) + 4*(i%4).
-    uint32_t v_rd[2];
+    // 4*(g/2) + i/4 (+ 16 per key chunk, + 8 for the upper half) and channels 32 db + 16*(g%2) +
+    // 4*(i%4), i.e. logical chunk 4 db + 2*(g%2) + (i%4)/2, byte 8*(i%2) inside it.
+    uint32_t v_rd[4];
     {
         const int i = lane & 15, gq = lane >> 4;
         const int row = 4 * (gq >> 1) + (i >> 2);
         const int u = 2 * (gq & 1) + ((i & 3) >> 1);
-        const int ph = u ^ v_swz(row);
-        v_rd[0] = lds0 + V_LDS_BASE + row * 256 + 16 * ph + 8 * (i & 1);
-        v_rd[1] = lds0 + V_LDS_BASE + row * 256 + 16 * (ph ^ 4) + 8 * (i & 1);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            v_rd[db] = lds0 + V_LDS_BASE + row * 256 + 16 * ((4 * db + u) ^ v_swz(row)) + 8 * (i & 1);
     }
-
-    auto qk = [&](auto bufc, f32x16_t (&s)[2]) {
-        constexpr int b = decltype(bufc)::value;
+    // K operand t (0..15) of the score product from K slot base kb (bytes): ks = t/2, block t%2.
+    auto k_operand = [&](uint32_t kb, int t) -> f16x8_t {
+        const int ks = t >> 1, mb = t & 1;
+        const uint32_t a = k_rd[ks] + kb + mb * 32 * 256;
+        return *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
+    };
+    // V operand of PV MFMA t (0..15) from V slot base vb: key chunk c = t/4, d block db = t%4.
+    auto v_operand = [&](uint32_t vb, int t) -> bf16x8_t {
+        const int c = t >> 2, db = t & 3;
+        const uint32_t a = v_rd[db] + vb + c * 16 * 256;
+        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
+        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 8 * 256));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // Keys of tile j past the end of the sequence get -inf (only the last tile can have any).
+    auto mask_tail = [&](int j, f32x16_t (&s)[2]) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[mb][i] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const uint32_t a = k_rd[ks & 3] + b * TILE_BYTES + (ks >> 2) * 128 + mb * 32 * 256;
-                f16x8_t op = *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op, qreg[ks], s[mb], 0, 0, 0);
+            for (int i = 0; i < 16; ++i) {
+                const int key = j * BN + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                if (key >= seg_len) s[mb][i] = -INFINITY;
             }
+    };
+    // Row max of a 64-key score tile (both lane halves).
+    auto row_max = [&](const f32x16_t (&s)[2]) -> float {
+        float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+        mx = fmaxf(mx, s[0][15]);
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+        return xhalf_max(mx);
     };
 
     f32x16_t oacc[4];
@@ -287,32 +325,30 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const bool ragged = (seg_len % BN) != 0;
     const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
-    // One tile step: softmax and PV of tile j (scores in sc) while the scores of tile j+1 are
-    // formed into sn and tile j+3 is copied into LDS.
+    // Scores of tile 0.
+    f32x16_t sa[2], sb[2];
+    {
+        f16x8_t ka[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) ka[t] = k_operand(0, t);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sa[mb][i] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+            sa[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sa[t & 1], 0, 0, 0);
+    }
+
+    // One tile step j (tile j in slot b): softmax weights and PV of tile j (scores sc) while the
+    // scores of tile j+1 (sn) are formed and tile j+PREF is fetched into slot (b+PREF) % NBUF.
     auto step = [&](auto bufc, int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
         constexpr int b = decltype(bufc)::value;
         constexpr int b1 = (b + 1) % NBUF;
-        constexpr int b3 = (b + 3) % NBUF;
-        const bool issue = j + 3 < ntiles;
-        if (issue) issue_tile(j + 3, b3);
-        if (j + 1 < ntiles) qk(Buf<b1>{}, sn);
-
-        if (ragged && j == ntiles - 1) {
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * BN + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key >= seg_len) sc[mb][i] = -INFINITY;
-                }
-        }
-        float mx = fmaxf(fmaxf(sc[0][0], sc[0][1]), sc[0][2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, sc[0][i]), sc[0][i + 1]);
-        mx = fmaxf(mx, sc[0][15]);
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, sc[1][i]), sc[1][i + 1]);
-        mx = xhalf_max(mx);
+        constexpr int bp = (b + PREF) % NBUF;
+        if (ragged && j == ntiles - 1) mask_tail(j, sc);
+        const float mx = row_max(sc);
+        // Lazy running max: rescale the accumulator only when this tile's max is well above it.
         const bool grow = mx > m_run + lazy_raw;
         if (__any(grow)) {
             const float m_new = grow ? mx : m_run;
@@ -325,48 +361,81 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
         }
         const float mneg = -m_run * sl2;
+
+        // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
+        // last tile the K slot holds stale data and these scores are discarded.
+        f16x8_t ka[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sn[mb][i] = 0.0f;
         bf16x8_t pb[4];
+        float lpart[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int mb = c >> 1, o = 8 * (c & 1);
             uint32_t u[4];
+            float ls = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[mb][o + 2 * e], sl2, mneg));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[mb][o + 2 * e + 1], sl2, mneg));
                 u[e] = pack_bf16x2(p0, p1);
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
-                                                        __builtin_bit_cast(bf16x2_t, one2), l_run, false);
+                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                     __builtin_bit_cast(bf16x2_t, one2), ls, false);
             }
+            lpart[c] = ls;
             pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
         }
+        l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int t = 0; t < 16; ++t)
+            sn[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sn[t & 1], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint32_t a = v_rd[db & 1] + b * TILE_BYTES + (db >> 1) * 128 + c * 16 * 256;
-                i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
-                i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 8 * 256));
-                const bf16x8_t op = __builtin_bit_cast(
-                    bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op, pb[c], oacc[db], 0, 0, 0);
-            }
+        for (int t = 0; t < 12; ++t) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
+        }
+
+        // Fetch tile j+PREF into the slot read last before the previous barrier.  Past the last
+        // tile the fetch repeats the last tile into that free slot (nothing reads it again);
+        // issuing unconditionally keeps the count of copies in flight fixed.
+        issue_tile(min(j + PREF, ntiles - 1), bp);
+
+        // PV of tile j.
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            const bf16x8_t va = v_operand(b * TILE_BYTES, t);
+            oacc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t >> 2], oacc[t & 3], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+#pragma unroll
+        for (int t = 0; t < 13; ++t) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 0);
+
         if constexpr (FUSED) {
-            if (issue) finish_tile(j + 3, b3);
+            finish_tile(min(j + PREF, ntiles - 1), bp);
             asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         } else {
-            // Tile j+2 (issued one step earlier) must have landed; tile j+3 may stay in flight.
-            if (issue) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
         }
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
     };
 
-    f32x16_t sa[2], sb[2];
-    qk(Buf<0>{}, sa);
     for (int j = 0; j < ntiles; j += 4) {
         step(Buf<0>{}, j, sa, sb);
         if (j + 1 >= ntiles) break;
@@ -376,6 +445,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         if (j + 3 >= ntiles) break;
         step(Buf<3>{}, j + 3, sb, sa);
     }
+    // Copies issued by the last steps (repeats of the last tile) must land before the
+    // workgroup's LDS is released.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
     const float inv = 1.0f / xhalf_sum(l_run);
