@@ -33,7 +33,8 @@ THETA = 10000.0
 SEED = 2000
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_bf16_wan13b_81f_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_kernel_wan13b_81f_traffic.txt")
+COPY_BYTES = 256 << 20       # device copy timed under the counters to scale FETCH_SIZE/WRITE_SIZE
 KERNEL_SOURCES = ["full_spatiotemporal_attention_amd/csrc/attn_bf16.hip",
                   "full_spatiotemporal_attention_amd/csrc/st_internal.h"]
 
@@ -50,17 +51,21 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(launch_flop_bytes_unused=None):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    counters were taken on a different version of the kernel source."""
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary (lines
+    ``key: value``), or None when the counters were taken on another version of the kernel."""
+    rec = {}
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                key, sep, val = line.partition(":")
+                if sep and key.strip() in ("kernel_source_hash", "hbm_bytes_per_launch"):
+                    rec[key.strip()] = val.strip()
+    except OSError:
         return None
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash() or "hbm_bytes_per_launch" not in rec:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return int(float(rec["hbm_bytes_per_launch"]))
 
 
 def cpu_baseline(rows_per_head: int):
@@ -102,9 +107,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=512, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip factorised and RoPE timings")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 256 MiB device-to-device copy first (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         eprint(f"bench.py --gpus {args.gpus}: this build runs on one GPU only (no sharding, no "
@@ -148,6 +155,14 @@ def main():
                                   sp, _lib.ST_BF16, ws.data_ptr(), wsb, out.data_ptr(), sh)
         if st:
             raise _lib.StError("st_attn3d_attend", st)
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -197,7 +212,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel",
+            "kernel": "attn_fwd_kernel<false>",
             "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
