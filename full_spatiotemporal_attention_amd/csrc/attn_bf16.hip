@@ -129,17 +129,6 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// HBM -> LDS copy of 16 bytes per lane: lane L's bytes from base + voff land at LDS byte address
-// lds + 16 L (global_load_lds_dwordx4, M0 = lds).  Written as inline asm so that the compiler does
-// not treat later LDS reads as waiting on it; the kernel waits for these copies explicitly with
-// s_waitcnt vmcnt before the barrier that publishes a tile.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff), "s"(base), "s"(lds)
-                 : "memory", "m0");
-}
-
 template <int B> using Buf = std::integral_constant<int, B>;
 
 // Instruction-class masks of __builtin_amdgcn_sched_group_barrier.

@@ -319,8 +319,8 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, o_s, table, g, heads,
                                         S, T, stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, o_s, (uint16_t*)out,
-                                          table, g, heads, stream);
+        e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, kt, o_s,
+                                          (uint16_t*)out, table, g, heads, stream);
     } else {
         float* o_s = (float*)(ws + table_bytes_for(T, H, W, rope_split));
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, o_s, table, g,

@@ -84,6 +84,17 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
     return (x < rem) ? x * (base + 1) + slot : rem * (base + 1) + (x - rem) * base + slot;
 }
 
+// HBM -> LDS copy of 16 bytes per lane: lane L's bytes from base + voff land at LDS byte address
+// lds + 16 L (global_load_lds_dwordx4, M0 = lds).  Written as inline asm so that the compiler does
+// not treat later LDS reads as waiting on it; callers wait for these copies explicitly with
+// s_waitcnt vmcnt before reading the data.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+
 // ------------------------------------------------------------------------------------------
 // Launchers (one per kernel family).  Each returns hipSuccess or the launch error.
 // ------------------------------------------------------------------------------------------
@@ -116,9 +127,9 @@ hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const ui
 
 // Factorised temporal stage, bf16, d = 128: for each spatial position s and head, the T rows
 // t * S + s attend to each other; values come from `vs` (the spatial stage's output).
-hipError_t launch_attn_temporal_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* vs,
-                                     uint16_t* out, const float2* table, const RopeGeom& g,
-                                     int heads, hipStream_t stream);
+hipError_t launch_attn_temporal_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* kt,
+                                     const uint16_t* vs, uint16_t* out, const float2* table,
+                                     const RopeGeom& g, int heads, hipStream_t stream);
 
 // fp32 checking kernel over row sets: sequence s holds rows s * base_mul + i * stride,
 // i < seq_len, for s < n_seqs.  Values from `v`, output rows written at the same indices.
