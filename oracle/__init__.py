@@ -9,11 +9,14 @@ from .st_oracle import (  # noqa: F401
     attention_dense,
     attention_rows,
     attn_flop_model,
+    cross_attention_ref,
     full_attention_ref,
     factorized_ref,
     latent_token_grid,
+    merge_partials_ref,
     metric_flops,
     factorized_flops,
+    partial_attention_ref,
     rope_frequencies,
     rope_pair_layout,
     rope3d_ref,

@@ -24,6 +24,15 @@ What it computes, and where each step comes from (page title, then section):
   length H'W'), then temporal attention at each spatial position (H'W' sequences of length T').
 * Cost model -- same section's per-layer formulas (full 4 (T' n_sp)^2 D, factorised
   T' 4 n_sp^2 D + n_sp 4 T'^2 D, linear 24 N D^2).
+* Text cross-attention -- "04 · HunyuanVideo 与 Wan", section 3.1 (one Wan block step by step):
+  queries come from the video tokens, keys and values from the text condition (at most 512
+  tokens, same section), and the text is not updated by this step.
+* Partial attention and its merge -- the CogVideoX record page ("Budget for that cost, because it
+  grows": attention is split across devices by context parallelism, 2D ring and Ulysses) and the
+  first page's shard listing under "Position: RoPE in three dimensions" (each device holds a
+  contiguous run of tokens whose (t, h, w) are absolute).  A device that sees only a run of keys
+  returns its normalised output and the log of its softmax denominator; the exact result over
+  all keys is their log-sum-exp weighted combination (the standard online-softmax identity).
 
 Readings where the pages are silent (each one is also listed in the design notes):
 
@@ -38,6 +47,9 @@ Readings where the pages are silent (each one is also listed in the design notes
   its values.
 * Absolute attention outputs on random inputs: PARITY UNPINNED (no page prints one); pinned by the
   special cases, invariants and an independent library routine in the tests.
+* Cross-attention applies no rotation: the page gives 3D RoPE for the video self-attention and none
+  for the text keys.  The log-sum-exp of a partial result is natural-log, over scaled scores
+  s / sqrt(d).
 """
 from __future__ import annotations
 
@@ -61,6 +73,9 @@ __all__ = [
     "attention_rows",
     "full_attention_ref",
     "factorized_ref",
+    "cross_attention_ref",
+    "partial_attention_ref",
+    "merge_partials_ref",
 ]
 
 
@@ -299,3 +314,62 @@ def factorized_ref(q, k, v, grid, split=(44, 42, 42), theta: float = 10000.0, ro
     if return_spatial:
         return out, o_s
     return out
+
+
+# --------------------------------------------------------------------------------------------
+# Next to the hot path: text cross-attention, partial attention over a run of keys, merge
+# --------------------------------------------------------------------------------------------
+
+def cross_attention_ref(q, k, v, rows=None) -> np.ndarray:
+    """Video queries against text keys and values: softmax(q k^T / sqrt(d)) v, no rotation.
+
+    q [Nq, heads, d], k and v [Nkv, heads, d]; returns [len(rows), heads, d] in float64.
+    """
+    if rows is None:
+        rows = np.arange(q.shape[0])
+    rows = np.asarray(rows)
+    qs = np.asarray(q[rows], ORACLE_DTYPE)
+    return attention_rows(qs, np.asarray(k, ORACLE_DTYPE), np.asarray(v, ORACLE_DTYPE))
+
+
+def partial_attention_ref(q, k, v, grid, n_text: int = 0, split=(44, 42, 42), theta: float = 10000.0,
+                          q_begin: int = 0, kv_begin: int = 0):
+    """Attention of a run of query rows against a run of key rows, with their global positions.
+
+    q holds global rows [q_begin, q_begin + len(q)), k and v hold rows [kv_begin, kv_begin +
+    len(k)) of the same T'H'W' + n_text sequence; each row is rotated by its own (t, h, w).
+    Returns (o, lse): o = softmax over this run of keys times v ([len(q), heads, d]) and
+    lse = log sum_j exp(s_j / sqrt(d)) over the run ([len(q), heads]), float64.
+    """
+    q = np.asarray(q, ORACLE_DTYPE)
+    k = np.asarray(k, ORACLE_DTYPE)
+    v = np.asarray(v, ORACLE_DTYPE)
+    qrows = np.arange(q_begin, q_begin + q.shape[0])
+    krows = np.arange(kv_begin, kv_begin + k.shape[0])
+    qr = rope3d_ref(q, grid, n_text, split, theta, rows=qrows)
+    kr = rope3d_ref(k, grid, n_text, split, theta, rows=krows)
+    d = q.shape[-1]
+    o = np.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=ORACLE_DTYPE)
+    lse = np.empty((q.shape[0], q.shape[1]), dtype=ORACLE_DTYPE)
+    for hd in range(q.shape[1]):
+        s = (qr[:, hd, :] @ kr[:, hd, :].T) / math.sqrt(d)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        den = e.sum(axis=1, keepdims=True)
+        o[:, hd, :] = (e / den) @ v[:, hd, :]
+        lse[:, hd] = (m + np.log(den))[:, 0]
+    return o, lse
+
+
+def merge_partials_ref(parts):
+    """Combine partial results (o_i, lse_i) over disjoint runs of keys into the result over all.
+
+    lse = log sum_i exp(lse_i) and o = sum_i exp(lse_i - lse) o_i, per row and head.
+    """
+    lses = np.stack([np.asarray(l, ORACLE_DTYPE) for _, l in parts])          # [P, N, heads]
+    m = lses.max(axis=0)
+    w = np.exp(lses - m)
+    tot = w.sum(axis=0)
+    lse = m + np.log(tot)
+    o = sum((w[i] / tot)[:, :, None] * np.asarray(parts[i][0], ORACLE_DTYPE) for i in range(len(parts)))
+    return o, lse

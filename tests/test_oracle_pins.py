@@ -535,3 +535,108 @@ def test_planted_cost_model_mistake_is_caught():
         r["factorized"] -= layers * s * 4 * t * t * hidden
         return r
     assert _fails(check_flop_table, no_temporal_term)
+
+
+# ---- text cross-attention, partial attention and merge -----------------------------------------
+
+def _sdpa64(q, k, v):
+    """torch SDPA in float64 on [N, heads, d] arrays (heads as the batch)."""
+    qt = torch.from_numpy(np.ascontiguousarray(np.transpose(q, (1, 0, 2))))
+    kt = torch.from_numpy(np.ascontiguousarray(np.transpose(k, (1, 0, 2))))
+    vt = torch.from_numpy(np.ascontiguousarray(np.transpose(v, (1, 0, 2))))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+    return np.transpose(o.numpy(), (1, 0, 2))
+
+
+def test_cross_attention_matches_torch_sdpa_rectangular():
+    rng = np.random.default_rng(71)
+    q = rng.standard_normal((37, 3, 16))
+    k = rng.standard_normal((11, 3, 16))
+    v = rng.standard_normal((11, 3, 16))
+    got = oracle.cross_attention_ref(q, k, v)
+    np.testing.assert_allclose(got, _sdpa64(q, k, v), rtol=1e-12, atol=1e-12)
+    rows = np.array([0, 5, 36])
+    np.testing.assert_allclose(oracle.cross_attention_ref(q, k, v, rows=rows), got[rows], rtol=0, atol=0)
+
+
+def test_cross_attention_single_key_returns_its_value_and_ignores_key_order():
+    rng = np.random.default_rng(72)
+    q = rng.standard_normal((5, 2, 8))
+    k = rng.standard_normal((1, 2, 8))
+    v = rng.standard_normal((1, 2, 8))
+    np.testing.assert_allclose(oracle.cross_attention_ref(q, k, v), np.broadcast_to(v, (5, 2, 8)), atol=1e-15)
+    k2 = rng.standard_normal((9, 2, 8))
+    v2 = rng.standard_normal((9, 2, 8))
+    perm = rng.permutation(9)
+    np.testing.assert_allclose(oracle.cross_attention_ref(q, k2, v2),
+                               oracle.cross_attention_ref(q, k2[perm], v2[perm]), rtol=1e-13, atol=1e-14)
+
+
+def _grid_inputs(seed, grid, n_text, heads, d):
+    rng = np.random.default_rng(seed)
+    n = grid[0] * grid[1] * grid[2] + n_text
+    return (rng.standard_normal((n, heads, d)), rng.standard_normal((n, heads, d)),
+            rng.standard_normal((n, heads, d)))
+
+
+def test_partial_over_all_keys_matches_sdpa_and_logsumexp():
+    grid, n_text, heads, d, split = (2, 3, 4), 3, 2, 16, (4, 6, 6)
+    q, k, v = _grid_inputs(73, grid, n_text, heads, d)
+    o, lse = oracle.partial_attention_ref(q, k, v, grid, n_text, split)
+    qr = oracle.rope3d_ref(q, grid, n_text, split)
+    kr = oracle.rope3d_ref(k, grid, n_text, split)
+    np.testing.assert_allclose(o, _sdpa64(qr, kr, v), rtol=1e-12, atol=1e-12)
+    s = torch.einsum("nhd,mhd->hnm", torch.from_numpy(qr), torch.from_numpy(kr)) / math.sqrt(d)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy().T, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_of_key_runs_equals_sdpa_over_all_keys():
+    grid, n_text, heads, d, split = (3, 2, 3), 2, 2, 16, (4, 6, 6)
+    q, k, v = _grid_inputs(74, grid, n_text, heads, d)
+    n = q.shape[0]
+    qb, qc = 4, 9                       # a run of queries with its global offset
+    cuts = [0, 5, 6, 13, n]             # uneven runs of keys, one of a single row
+    parts = [oracle.partial_attention_ref(q[qb:qb + qc], k[a:b], v[a:b], grid, n_text, split,
+                                          q_begin=qb, kv_begin=a) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = oracle.merge_partials_ref(parts)
+    qr = oracle.rope3d_ref(q, grid, n_text, split)[qb:qb + qc]
+    kr = oracle.rope3d_ref(k, grid, n_text, split)
+    np.testing.assert_allclose(o, _sdpa64(qr, kr, v), rtol=1e-12, atol=1e-12)
+    s = torch.einsum("nhd,mhd->hnm", torch.from_numpy(qr), torch.from_numpy(kr)) / math.sqrt(d)
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy().T, rtol=1e-12, atol=1e-12)
+    # order of the parts does not matter; one part merges to itself
+    o2, lse2 = oracle.merge_partials_ref(parts[::-1])
+    np.testing.assert_allclose(o2, o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-14)
+    o1, l1 = oracle.merge_partials_ref(parts[:1])
+    np.testing.assert_allclose(o1, parts[0][0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(l1, parts[0][1], rtol=0, atol=1e-15)
+
+
+def test_partial_uses_global_positions():
+    """The same key rows give different results when their global offset changes (RoPE)."""
+    grid, heads, d, split = (4, 2, 2), 1, 8, (4, 2, 2)
+    q, k, v = _grid_inputs(75, grid, 0, heads, d)
+    a = oracle.partial_attention_ref(q[:4], k[4:8], v[4:8], grid, 0, split, q_begin=0, kv_begin=4)
+    b = oracle.partial_attention_ref(q[:4], k[4:8], v[4:8], grid, 0, split, q_begin=0, kv_begin=8)
+    assert np.abs(a[1] - b[1]).max() > 1e-3
+
+
+@pytest.mark.parametrize("mode", ["no_shift", "lse_base2", "unweighted"])
+def test_planted_merge_mistakes_are_caught(mode):
+    grid, n_text, heads, d, split = (2, 2, 3), 0, 2, 8, (4, 2, 2)
+    q, k, v = _grid_inputs(76, grid, n_text, heads, d)
+    parts = [oracle.partial_attention_ref(q, k[a:b], v[a:b], grid, n_text, split, kv_begin=a)
+             for a, b in [(0, 5), (5, 12)]]
+    lses = np.stack([l for _, l in parts])
+    if mode == "no_shift":
+        w = np.exp(lses)
+        o = sum(w[i][:, :, None] * parts[i][0] for i in range(2))
+    elif mode == "lse_base2":
+        w = 2.0 ** lses
+        o = sum((w[i] / w.sum(0))[:, :, None] * parts[i][0] for i in range(2))
+    else:
+        o = 0.5 * (parts[0][0] + parts[1][0])
+    qr = oracle.rope3d_ref(q, grid, n_text, split)
+    kr = oracle.rope3d_ref(k, grid, n_text, split)
+    assert np.abs(o - _sdpa64(qr, kr, v)).max() > 1e-3
