@@ -270,6 +270,39 @@ def main():
         fused_ms = e0.elapsed_time(e1) / reps
         extras["fused_rope_step_ms"] = round(fused_ms, 4)
         extras["fused_rope_TFLOPs"] = round(flop / (fused_ms * 1e-3) / 1e12, 2)
+        # Text cross-attention next to the self-attention (Wan: at most 512 text tokens).
+        n_txt = 512
+        kt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=torch.Generator(device=dev).manual_seed(SEED + 20)).to(torch.bfloat16)
+        vt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=torch.Generator(device=dev).manual_seed(SEED + 21)).to(torch.bfloat16)
+        cws = torch.empty(max(256, fa._lib.load().st_attn_cross_workspace_bytes(n, n_txt, HEADS, D, _lib.ST_BF16)),
+                          dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            fa.attn_cross(q, kt_, vt_, out=fout, workspace=cws)
+        e0.record(stream)
+        for _ in range(reps):
+            fa.attn_cross(q, kt_, vt_, out=fout, workspace=cws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cross_ms = e0.elapsed_time(e1) / reps
+        cross_flop = 4.0 * n * n_txt * HEADS * D
+        extras["cross_512_ms"] = round(cross_ms, 4)
+        extras["cross_512_TFLOPs"] = round(cross_flop / (cross_ms * 1e-3) / 1e12, 2)
+        # Merge of two partial results over the whole grid (HBM-bound: 2 reads + 1 write of O).
+        lse_a = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
+        lse_b = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
+        mo = torch.empty_like(q)
+        ml = torch.empty_like(lse_a)
+        for _ in range(2):
+            fa.attn_merge([(out, lse_a), (fout, lse_b)], out=mo, lse_out=ml)
+        e0.record(stream)
+        for _ in range(reps):
+            fa.attn_merge([(out, lse_a), (fout, lse_b)], out=mo, lse_out=ml)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        merge_ms = e0.elapsed_time(e1) / reps
+        merge_bytes = 3.0 * q.numel() * 2 + 3.0 * n * HEADS * 4
+        extras["merge2_ms"] = round(merge_ms, 4)
+        extras["merge2_GBps"] = round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)
         result["extras"] = extras
         eprint(f"extras: {extras}")
 

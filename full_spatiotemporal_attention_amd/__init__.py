@@ -19,6 +19,9 @@ __all__ = [
     "attn3d_stage",
     "attn3d_attend",
     "attn_factorized",
+    "attn_cross",
+    "attn3d_partial",
+    "attn_merge",
     "rope3d_apply",
     "rope3d_table",
     "attn3d_workspace_bytes",
@@ -213,3 +216,83 @@ def rope3d_apply(x, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
                              ws.data_ptr(), ws.numel() * ws.element_size(), _stream(x.device))
     _lib.check("st_rope3d_apply", st)
     return out
+
+
+def attn_cross(q, k, v, out=None, workspace=None) -> torch.Tensor:
+    """Text cross-attention: softmax(q k^T / sqrt(d)) v, q [Nq, heads, d], k/v [Nkv, heads, d]."""
+    lib = _lib.load()
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError("expected contiguous [rows, heads, d] GPU tensors")
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("tensors must share device and dtype")
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [Nkv, heads, d] with the heads and d of q")
+    n_q, heads, d = q.shape
+    n_kv = k.shape[0]
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = int(lib.st_attn_cross_workspace_bytes(n_q, n_kv, heads, d, code))
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib.st_attn_cross_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), n_q, n_kv, heads, d, code,
+                               ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
+                               _stream(q.device))
+    _lib.check("st_attn_cross_fwd", st)
+    return out
+
+
+def attn3d_partial(q, k, v, grid, q_begin=0, kv_begin=0, n_text=0, rope_split=WAN_SPLIT,
+                   theta=10000.0, workspace=None):
+    """Attention of global query rows [q_begin, +len(q)) against key rows [kv_begin, +len(k)).
+
+    Returns (out, lse): the softmax-normalised output over this run of keys and the float32
+    log-sum-exp of the scaled scores, [len(q), heads].
+    """
+    lib = _lib.load()
+    T, H, W = (int(x) for x in grid)
+    for t in (q, k, v):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError("expected contiguous [rows, heads, d] GPU tensors")
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [Nkv, heads, d] with the heads and d of q")
+    q_count, heads, d = q.shape
+    kv_count = k.shape[0]
+    code = _dtype_code(q)
+    sp = _lib.split_arg(rope_split)
+    out = torch.empty_like(q)
+    lse = torch.empty((q_count, heads), dtype=torch.float32, device=q.device)
+    nbytes = int(lib.st_attn3d_partial_workspace_bytes(T, H, W, int(n_text), heads, d, sp, code, kv_count))
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib.st_attn3d_partial_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads,
+                                   d, sp, float(theta), code, int(q_begin), q_count, int(kv_begin),
+                                   kv_count, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                   out.data_ptr(), lse.data_ptr(), _stream(q.device))
+    _lib.check("st_attn3d_partial_fwd", st)
+    return out, lse
+
+
+def attn_merge(parts, out=None, lse_out=None):
+    """Merge [(o_i, lse_i), ...] over disjoint key runs; returns (out, lse)."""
+    import ctypes
+    lib = _lib.load()
+    if not parts:
+        raise ValueError("no parts")
+    o0, l0 = parts[0]
+    n_rows, heads, d = o0.shape
+    for o, l in parts:
+        if o.shape != o0.shape or o.dtype != o0.dtype or not o.is_contiguous():
+            raise ValueError("parts must share shape and dtype")
+        if l.shape != (n_rows, heads) or l.dtype != torch.float32 or not l.is_contiguous():
+            raise ValueError("lse parts must be contiguous float32 [rows, heads]")
+    if out is None:
+        out = torch.empty_like(o0)
+    if lse_out is None:
+        lse_out = torch.empty_like(l0)
+    n = len(parts)
+    optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o, _ in parts])
+    lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for _, l in parts])
+    st = lib.st_attn_merge(n, optr, lptr, n_rows, heads, d, _dtype_code(o0), out.data_ptr(),
+                           lse_out.data_ptr(), _stream(o0.device))
+    _lib.check("st_attn_merge", st)
+    return out, lse_out

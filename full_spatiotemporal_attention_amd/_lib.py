@@ -35,6 +35,12 @@ SIGNATURES = {
     "st_attn_factorized_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _split, _i]),
     "st_attn_factorized_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p]),
     "st_rope3d_apply": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p]),
+    "st_attn_cross_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "st_attn_cross_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p, _p]),
+    "st_attn3d_partial_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _split, _i, _i]),
+    "st_attn3d_partial_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _i, _i, _i, _i,
+                                   _p, _sz, _p, _p, _p]),
+    "st_attn_merge": (_i, [_i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _i, _i, _i, _p, _p, _p]),
     "st_status_str": (ctypes.c_char_p, [_i]),
     "st_last_hip_error": (_i, []),
     "st_version": (ctypes.c_char_p, []),

@@ -72,8 +72,12 @@ struct AttnParams {
     const float2* table;
     RopeGeom g;
     int heads;
-    int seg_len;
+    float* lse;            // optional [q rows][heads] log-sum-exp of the scaled scores
+    int seg_len;           // key (and value) rows per sequence
+    int q_len;             // query rows per sequence
     int n_segs;
+    int q_pos_base;        // global row (for positions) of query buffer row 0
+    int kv_pos_base;       // global row of key buffer row 0
     int q_tiles;
     int k_tiles;
     int total_wg;
@@ -88,6 +92,7 @@ struct PrepParams {
     int heads;
     int seg_len;
     int n_segs;
+    int kv_pos_base;
     int k_tiles;
 };
 
@@ -146,8 +151,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const int rest = logical / p.q_tiles;
     const int seg = rest % p.n_segs;
     const int head = rest / p.n_segs;
-    const int seg_base = seg * p.seg_len;
+    const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
     const int seg_len = p.seg_len;
+    const int q_len = p.q_len;
     const long long row_stride = (long long)p.heads * D;
     const int ntiles = p.k_tiles;
 
@@ -206,7 +212,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = fkr + 32 * i;
-                const int n = seg_base + j * BN + r;
+                const int n = p.kv_pos_base + seg_base + j * BN + r;
                 int t = 0, h = 0, w = 0;
                 const bool text = n >= g.Nv;
                 if (!text) decode_pos(n, g, t, h, w);
@@ -229,13 +235,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     }
 
     const int q_local = qt * BM + wave * 32 + l32;
-    const bool q_valid = q_local < seg_len;
-    const int q_row = seg_base + (q_valid ? q_local : 0);
+    const bool q_valid = q_local < q_len;
+    const int q_row = seg * q_len + (q_valid ? q_local : 0);   // query buffer row
+    const int q_pos = p.q_pos_base + q_row;                    // its global row
     f16x8_t qreg[8];
     {
         int t = 0, h = 0, w = 0;
-        const bool text = q_row >= g.Nv;
-        if (!text) decode_pos(q_row, g, t, h, w);
+        const bool text = q_pos >= g.Nv;
+        if (!text) decode_pos(q_pos, g, t, h, w);
         const uint16_t* qp = p.q + q_row * row_stride + (long long)head * D;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
@@ -439,7 +446,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
-    const float inv = 1.0f / xhalf_sum(l_run);
+    const float l_tot = xhalf_sum(l_run);
+    const float inv = 1.0f / l_tot;
+    if (p.lse && q_valid && hh == 0)
+        p.lse[(long long)q_row * p.heads + head] = m_run * (sl2 * 0.6931471805599453f) + __logf(l_tot);
     if (q_valid) {
         uint16_t* op = p.out + q_row * row_stride + (long long)head * D;
 #pragma unroll
@@ -472,8 +482,9 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
         const int r = id >> 4, c = id & 15;
         const int kl = kt * BN + r;
         const bool valid = kl < p.seg_len;
-        const int n = seg * p.seg_len + (valid ? kl : 0);
-        uint4 raw = valid ? ld16(p.k + n * row_stride + (long long)head * D + 8 * c) : make_uint4(0, 0, 0, 0);
+        const int nb = seg * p.seg_len + (valid ? kl : 0);   // key buffer row
+        const int n = p.kv_pos_base + nb;                    // its global row
+        uint4 raw = valid ? ld16(p.k + nb * row_stride + (long long)head * D + 8 * c) : make_uint4(0, 0, 0, 0);
         int t = 0, h = 0, w = 0;
         const bool text = n >= g.Nv;
         if (!text) decode_pos(n, g, t, h, w);
@@ -482,20 +493,25 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
 }
 
 AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* out,
-                       const float2* table, const RopeGeom& g, int heads, int seg_len, int n_segs) {
+                       float* lse, const float2* table, const RopeGeom& g, int heads,
+                       const SeqLayout& L) {
     AttnParams p;
     p.q = q;
     p.k = k;
     p.v = v;
     p.out = out;
+    p.lse = lse;
     p.table = table;
     p.g = g;
     p.heads = heads;
-    p.seg_len = seg_len;
-    p.n_segs = n_segs;
-    p.q_tiles = (seg_len + BM - 1) / BM;
-    p.k_tiles = (seg_len + BN - 1) / BN;
-    p.total_wg = p.q_tiles * n_segs * heads;
+    p.seg_len = L.kv_len;
+    p.q_len = L.q_len;
+    p.n_segs = L.n_segs;
+    p.q_pos_base = L.q_pos_base;
+    p.kv_pos_base = L.kv_pos_base;
+    p.q_tiles = (L.q_len + BM - 1) / BM;
+    p.k_tiles = (L.kv_len + BN - 1) / BN;
+    p.total_wg = p.q_tiles * L.n_segs * heads;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     return p;
 }
@@ -508,37 +524,40 @@ hipError_t launch(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-size_t attn_stage_elems(int heads, int seg_len, int n_segs) {
-    const size_t k_tiles = (size_t)(seg_len + BN - 1) / BN;
+size_t attn_stage_elems(int heads, int kv_len, int n_segs) {
+    const size_t k_tiles = (size_t)(kv_len + BN - 1) / BN;
     return (size_t)heads * n_segs * k_tiles * BN * D;
 }
 
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
-                         int heads, int seg_len, int n_segs, hipStream_t stream) {
+                         int heads, const SeqLayout& L, hipStream_t stream) {
     PrepParams p;
     p.k = k;
     p.kt = kt;
     p.table = table;
     p.g = g;
     p.heads = heads;
-    p.seg_len = seg_len;
-    p.n_segs = n_segs;
-    p.k_tiles = (seg_len + BN - 1) / BN;
-    const int blocks = heads * n_segs * p.k_tiles;
+    p.seg_len = L.kv_len;
+    p.n_segs = L.n_segs;
+    p.kv_pos_base = L.kv_pos_base;
+    p.k_tiles = (L.kv_len + BN - 1) / BN;
+    const int blocks = heads * L.n_segs * p.k_tiles;
     hipLaunchKernelGGL(k_prep_kernel, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
-                                   uint16_t* out, const float2* table, const RopeGeom& g,
-                                   int heads, int seg_len, int n_segs, hipStream_t stream) {
-    return launch<false>(make_params(q, kt, v, out, table, g, heads, seg_len, n_segs), stream);
+                                   uint16_t* out, float* lse, const float2* table,
+                                   const RopeGeom& g, int heads, const SeqLayout& L,
+                                   hipStream_t stream) {
+    return launch<false>(make_params(q, kt, v, out, lse, table, g, heads, L), stream);
 }
 
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                  uint16_t* out, const float2* table, const RopeGeom& g,
-                                  int heads, int seg_len, int n_segs, hipStream_t stream) {
-    return launch<true>(make_params(q, k, v, out, table, g, heads, seg_len, n_segs), stream);
+                                  uint16_t* out, float* lse, const float2* table,
+                                  const RopeGeom& g, int heads, const SeqLayout& L,
+                                  hipStream_t stream) {
+    return launch<true>(make_params(q, k, v, out, lse, table, g, heads, L), stream);
 }
 
 }  // namespace st

@@ -20,13 +20,12 @@ struct F32Params {
     const float* k;
     const float* v;
     float* out;
+    float* lse;
     const float2* table;
     RopeGeom g;
     int heads;
     int d;
-    int seq_len;
-    int base_mul;
-    int stride;
+    F32Layout L;
     float scale;
 };
 
@@ -48,15 +47,17 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
     const int half = d >> 1;
     const long long rs = (long long)p.heads * d;
     const RopeGeom& g = p.g;
-    const int seq0 = seq * p.base_mul;
+    const F32Layout& L = p.L;
+    const int q0 = seq * L.q_mul;
+    const int kv0 = seq * L.kv_mul;
 
     const int qi = blockIdx.x * QB + tid;
-    const bool qv = qi < p.seq_len;
-    const int qrow = seq0 + (qv ? qi : 0) * p.stride;
+    const bool qv = qi < L.q_len;
+    const int qrow = q0 + (qv ? qi : 0) * L.q_stride;   // query buffer row
     {
         int t, h, w;
         bool text;
-        row_pos(qrow, g, t, h, w, text);
+        row_pos(L.q_pos_base + qrow, g, t, h, w, text);
         const float* qp = p.q + qrow * rs + (long long)head * d;
         for (int pp = 0; pp < half; ++pp) {
             float2 x = qv ? *reinterpret_cast<const float2*>(qp + 2 * pp) : make_float2(0.f, 0.f);
@@ -71,16 +72,16 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
     for (int c = 0; c < DMAX; ++c) o[c] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int k0 = 0; k0 < p.seq_len; k0 += KB) {
-        const int nk = min(KB, p.seq_len - k0);
+    for (int k0 = 0; k0 < L.kv_len; k0 += KB) {
+        const int nk = min(KB, L.kv_len - k0);
         __syncthreads();
         for (int idx = tid; idx < nk * half; idx += QB) {
             const int r = idx / half;
             const int pp = idx - r * half;
-            const int krow = seq0 + (k0 + r) * p.stride;
+            const int krow = kv0 + (k0 + r) * L.kv_stride;   // key buffer row
             int t, h, w;
             bool text;
-            row_pos(krow, g, t, h, w, text);
+            row_pos(L.kv_pos_base + krow, g, t, h, w, text);
             const long long base = krow * rs + (long long)head * d + 2 * pp;
             float2 x = *reinterpret_cast<const float2*>(p.k + base);
             rotate_pair(x.x, x.y, p.table[pair_entry(pp, t, h, w, text, g)]);
@@ -126,6 +127,7 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
         }
     }
 
+    if (qv && p.lse) p.lse[(long long)qrow * p.heads + head] = m_run + logf(l_run);
     if (qv) {
         const float inv = 1.0f / l_run;
         float* op = p.out + qrow * rs + (long long)head * d;
@@ -137,23 +139,22 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
 
 }  // namespace
 
-hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            const float2* table, const RopeGeom& g, int heads, int d,
-                           int n_seqs, int seq_len, int base_mul, int stride, hipStream_t stream) {
+                           const F32Layout& L, hipStream_t stream) {
     F32Params p;
     p.q = q;
     p.k = k;
     p.v = v;
     p.out = out;
+    p.lse = lse;
     p.table = table;
     p.g = g;
     p.heads = heads;
     p.d = d;
-    p.seq_len = seq_len;
-    p.base_mul = base_mul;
-    p.stride = stride;
+    p.L = L;
     p.scale = 1.0f / sqrtf((float)d);
-    dim3 grid((seq_len + QB - 1) / QB, n_seqs, heads);
+    dim3 grid((L.q_len + QB - 1) / QB, L.n_seqs, heads);
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(QB), 0, stream, p);
     return hipGetLastError();
 }

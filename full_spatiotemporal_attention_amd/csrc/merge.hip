@@ -1,0 +1,128 @@
+// Merge of partial attention results over disjoint runs of keys.
+//
+// Context parallelism splits the keys of one long sequence across devices (the CogVideoX record
+// page, "Budget for that cost, because it grows": 2D ring and Ulysses); a device that saw one run
+// of keys holds o_i = softmax over that run times v and lse_i = log sum over the run of
+// exp(s / sqrt(d)).  The result over all keys is lse = log sum_i exp(lse_i) and
+// o = sum_i exp(lse_i - lse) o_i, per (row, head).  HBM-bound: each part is read once, the
+// output written once.
+//
+// Thread layout: the channels of one (row, head) are spread over a power-of-two group of lanes
+// (16 bytes per lane) inside one wavefront, so every lane of the group has read the lse values
+// before any lane writes: out and lse_out may alias any part (an in-place running merge).
+#include "st_internal.h"
+
+namespace st {
+namespace {
+
+template <typename T>
+struct MergeParams {
+    const T* o[kMaxMergeParts];
+    const float* lse[kMaxMergeParts];
+    int n_parts;
+    long long rows_heads;
+    int d;
+    int chunks;        // 16-byte chunks per (row, head)
+    int group_log2;    // lanes per (row, head) = 1 << group_log2 >= chunks
+    T* out;
+    float* lse_out;
+};
+
+__device__ __forceinline__ void load_chunk(const uint16_t* p, float (&x)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+__device__ __forceinline__ void store_chunk(uint16_t* p, const float (&x)[8]) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+}
+__device__ __forceinline__ void load_chunk(const float* p, float (&x)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+}
+__device__ __forceinline__ void store_chunk(float* p, const float (&x)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+template <typename T, int E>
+__global__ void __launch_bounds__(256) merge_kernel(MergeParams<T> p) {
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rh = tid >> p.group_log2;
+    const int c = (int)(tid & ((1 << p.group_log2) - 1));
+    if (rh >= p.rows_heads) return;
+    float m = -INFINITY;
+    float l[kMaxMergeParts];
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+        l[i] = i < p.n_parts ? p.lse[i][rh] : -INFINITY;
+        m = fmaxf(m, l[i]);
+    }
+    float tot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+        l[i] = (i < p.n_parts && m > -INFINITY) ? expf(l[i] - m) : 0.0f;
+        tot += l[i];
+    }
+    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+    if (c < p.chunks) {
+        float acc[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+        const long long off = rh * p.d + (long long)c * E;
+#pragma unroll
+        for (int i = 0; i < kMaxMergeParts; ++i) {
+            if (i < p.n_parts) {
+                float x[E];
+                load_chunk(p.o[i] + off, x);
+                const float w = l[i] * inv;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[e], acc[e]);
+            }
+        }
+        store_chunk(p.out + off, acc);
+    }
+    if (c == 0 && p.lse_out) p.lse_out[rh] = tot > 0.0f ? m + logf(tot) : -INFINITY;
+}
+
+template <typename T, int E>
+hipError_t launch_merge(int n_parts, const T* const* o, const float* const* lse, long long rows_heads,
+                        int d, T* out, float* lse_out, hipStream_t stream) {
+    MergeParams<T> p;
+    for (int i = 0; i < kMaxMergeParts; ++i) {
+        p.o[i] = i < n_parts ? o[i] : nullptr;
+        p.lse[i] = i < n_parts ? lse[i] : nullptr;
+    }
+    p.n_parts = n_parts;
+    p.rows_heads = rows_heads;
+    p.d = d;
+    p.chunks = d / E;
+    p.group_log2 = 0;
+    while ((1 << p.group_log2) < p.chunks) ++p.group_log2;
+    p.out = out;
+    p.lse_out = lse_out;
+    const long long threads = rows_heads << p.group_log2;
+    const long long blocks = (threads + 255) / 256;
+    hipLaunchKernelGGL((merge_kernel<T, E>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge_bf16(int n_parts, const uint16_t* const* o, const float* const* lse,
+                             long long rows_heads, int d, uint16_t* out, float* lse_out,
+                             hipStream_t stream) {
+    return launch_merge<uint16_t, 8>(n_parts, o, lse, rows_heads, d, out, lse_out, stream);
+}
+
+hipError_t launch_merge_f32(int n_parts, const float* const* o, const float* const* lse,
+                            long long rows_heads, int d, float* out, float* lse_out,
+                            hipStream_t stream) {
+    return launch_merge<float, 4>(n_parts, o, lse, rows_heads, d, out, lse_out, stream);
+}
+
+}  // namespace st

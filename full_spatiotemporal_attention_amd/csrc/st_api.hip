@@ -107,6 +107,32 @@ st_status check_attn(const void* q, const void* k, const void* v, const void* ou
     return ST_OK;
 }
 
+// One problem of n query rows against the same n key rows (full attention).
+st::SeqLayout self_layout(int n) {
+    st::SeqLayout L;
+    L.n_segs = 1;
+    L.q_len = n;
+    L.kv_len = n;
+    L.q_pos_base = 0;
+    L.kv_pos_base = 0;
+    return L;
+}
+
+st::F32Layout f32_layout(int n_seqs, int q_len, int q_mul, int q_stride, int kv_len, int kv_mul,
+                         int kv_stride, int q_pos_base = 0, int kv_pos_base = 0) {
+    st::F32Layout L;
+    L.n_seqs = n_seqs;
+    L.q_len = q_len;
+    L.q_mul = q_mul;
+    L.q_stride = q_stride;
+    L.q_pos_base = q_pos_base;
+    L.kv_len = kv_len;
+    L.kv_mul = kv_mul;
+    L.kv_stride = kv_stride;
+    L.kv_pos_base = kv_pos_base;
+    return L;
+}
+
 st_status hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
     return ST_ERR_HIP;
@@ -194,8 +220,8 @@ st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int he
     float2* table = (float2*)ws;
     hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
     if (e != hipSuccess) return hip_fail(e);
-    e = st::launch_k_prep((const uint16_t*)k, (uint16_t*)(ws + L.table_bytes), table, g, heads, (int)n,
-                          1, stream);
+    e = st::launch_k_prep((const uint16_t*)k, (uint16_t*)(ws + L.table_bytes), table, g, heads,
+                          self_layout((int)n), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -215,8 +241,8 @@ st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, in
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
     const char* ws = (const char*)workspace;
     hipError_t e = st::launch_attn_bf16_staged((const uint16_t*)q, (const uint16_t*)(ws + L.table_bytes),
-                                               (const uint16_t*)v, (uint16_t*)out, (const float2*)ws, g,
-                                               heads, (int)n, 1, stream);
+                                               (const uint16_t*)v, (uint16_t*)out, nullptr,
+                                               (const float2*)ws, g, heads, self_layout((int)n), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -245,8 +271,8 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int 
     float2* table = (float2*)workspace;
     hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
     if (e != hipSuccess) return hip_fail(e);
-    e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, table, g,
-                            heads, d, 1, (int)n, 0, 1, stream);
+    e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
+                            table, g, heads, d, f32_layout(1, (int)n, 0, 1, (int)n, 0, 1), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -269,10 +295,11 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T
     if (e != hipSuccess) return hip_fail(e);
     if (dtype == ST_BF16)
         e = st::launch_attn_bf16_fused((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
-                                       (uint16_t*)out, table, g, heads, (int)n, 1, stream);
+                                       (uint16_t*)out, nullptr, table, g, heads, self_layout((int)n),
+                                       stream);
     else
-        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, table,
-                                g, heads, d, 1, (int)n, 0, 1, stream);
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
+                                table, g, heads, d, f32_layout(1, (int)n, 0, 1, (int)n, 0, 1), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -314,20 +341,26 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
         StageLayout L = stage_layout(T, H, W, heads, S, T, rope_split);
         uint16_t* kt = (uint16_t*)(ws + L.table_bytes);
         uint16_t* o_s = (uint16_t*)(ws + L.total);
-        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, S, T, stream);
+        st::SeqLayout SL;
+        SL.n_segs = T;
+        SL.q_len = S;
+        SL.kv_len = S;
+        SL.q_pos_base = 0;
+        SL.kv_pos_base = 0;
+        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, SL, stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, o_s, table, g, heads,
-                                        S, T, stream);
+        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, o_s, nullptr, table,
+                                        g, heads, SL, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, kt, o_s,
                                           (uint16_t*)out, table, g, heads, stream);
     } else {
         float* o_s = (float*)(ws + table_bytes_for(T, H, W, rope_split));
-        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, o_s, table, g,
-                                heads, d, T, S, S, 1, stream);
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, o_s, nullptr, table,
+                                g, heads, d, f32_layout(T, S, S, 1, S, S, 1), stream);
         if (e != hipSuccess) return hip_fail(e);
-        e = st::launch_attn_f32((const float*)q, (const float*)k, o_s, (float*)out, table, g, heads,
-                                d, S, T, 1, S, stream);
+        e = st::launch_attn_f32((const float*)q, (const float*)k, o_s, (float*)out, nullptr, table, g,
+                                heads, d, f32_layout(S, T, 1, S, T, 1, S), stream);
     }
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
@@ -364,6 +397,183 @@ st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_tex
     else
         e = st::launch_rope_apply_f32((const float*)x, (float*)y, g, (int)n, heads, d, table,
                                       stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+// ---- text cross-attention --------------------------------------------------------------------
+
+size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dtype dtype) {
+    if (n_q < 1 || n_kv < 1 || n_q >= kMaxRows || n_kv >= kMaxRows || heads < 1 || heads > 65535)
+        return 0;
+    const size_t table = align_up(sizeof(float2), kWsAlign);
+    if (dtype == ST_F32) return (d >= 2 && !(d & 1) && d <= 128) ? table : 0;
+    if (dtype != ST_BF16 || d != 128) return 0;
+    return table + align_up(st::attn_stage_elems(heads, n_kv, 1) * 2, kWsAlign);
+}
+
+st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,
+                            int heads, int d, st_dtype dtype, void* workspace, size_t ws_bytes,
+                            void* out, hipStream_t stream) {
+    if (!q || !k || !v || !out || !workspace) return ST_ERR_NULL;
+    if (n_q < 1 || n_kv < 1 || n_q >= kMaxRows || n_kv >= kMaxRows) return ST_ERR_SHAPE;
+    if (heads < 1 || heads > 65535 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
+    if (dtype == ST_BF16) {
+        if (d != 128) return ST_ERR_UNSUPPORTED;
+    } else if (dtype == ST_F32) {
+        if (d > 128) return ST_ERR_UNSUPPORTED;
+    } else {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+        return ST_ERR_ALIGN;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    const size_t qb = (size_t)n_q * heads * d * elem_size(dtype);
+    const size_t kb = (size_t)n_kv * heads * d * elem_size(dtype);
+    if (overlaps(out, qb, q, qb) || overlaps(out, qb, k, kb) || overlaps(out, qb, v, kb))
+        return ST_ERR_ALIAS;
+    if (ws_bytes < st_attn_cross_workspace_bytes(n_q, n_kv, heads, d, dtype)) return ST_ERR_WORKSPACE;
+    if (overlaps(workspace, ws_bytes, q, qb) || overlaps(workspace, ws_bytes, out, qb) ||
+        overlaps(workspace, ws_bytes, k, kb) || overlaps(workspace, ws_bytes, v, kb))
+        return ST_ERR_ALIAS;
+    // A geometry with no video rows: every row is left unrotated (the identity table entry).
+    const int none[3] = {0, 0, 0};
+    st::RopeGeom g = st::make_geom(1, 1, 1, none);
+    g.Nv = 0;
+    char* ws = (char*)workspace;
+    float2* table = (float2*)ws;
+    hipError_t e = st::launch_rope_table(g, 10000.0, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dtype == ST_BF16) {
+        st::SeqLayout L;
+        L.n_segs = 1;
+        L.q_len = n_q;
+        L.kv_len = n_kv;
+        L.q_pos_base = 0;
+        L.kv_pos_base = 0;
+        uint16_t* kt = (uint16_t*)(ws + align_up(sizeof(float2), kWsAlign));
+        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out,
+                                        nullptr, table, g, heads, L, stream);
+    } else {
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
+                                table, g, heads, d, f32_layout(1, n_q, 0, 1, n_kv, 0, 1), stream);
+    }
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+// ---- partial attention over a run of keys, and the merge -----------------------------------------
+
+size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
+                                         const int rope_split[3], st_dtype dtype, int kv_count) {
+    long long n = 0;
+    if (!rope_split || !grid_ok(T, H, W, n_text, &n) || heads < 1 || heads > 65535) return 0;
+    if (check_split(rope_split, d) != ST_OK) return 0;
+    if (kv_count < 1 || kv_count > n) return 0;
+    if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) : 0;
+    if (dtype != ST_BF16 || d != 128) return 0;
+    return stage_layout(T, H, W, heads, kv_count, 1, rope_split).total;
+}
+
+st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                                int n_text, int heads, int d, const int rope_split[3], float theta,
+                                st_dtype dtype, int q_begin, int q_count, int kv_begin,
+                                int kv_count, void* workspace, size_t ws_bytes, void* out,
+                                float* lse, hipStream_t stream) {
+    if (!q || !k || !v || !out || !lse || !workspace || !rope_split) return ST_ERR_NULL;
+    long long n = 0;
+    if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
+    if (heads < 1 || heads > 65535 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
+    if (q_begin < 0 || q_count < 1 || (long long)q_begin + q_count > n) return ST_ERR_SHAPE;
+    if (kv_begin < 0 || kv_count < 1 || (long long)kv_begin + kv_count > n) return ST_ERR_SHAPE;
+    st_status s = check_split(rope_split, d);
+    if (s != ST_OK) return s;
+    if (dtype == ST_BF16) {
+        if (d != 128) return ST_ERR_UNSUPPORTED;
+    } else if (dtype == ST_F32) {
+        if (d > 128) return ST_ERR_UNSUPPORTED;
+    } else {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+        return ST_ERR_ALIGN;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    const size_t qb = (size_t)q_count * heads * d * elem_size(dtype);
+    const size_t kb = (size_t)kv_count * heads * d * elem_size(dtype);
+    const size_t lb = (size_t)q_count * heads * sizeof(float);
+    const void* ins[3] = {q, k, v};
+    const size_t insz[3] = {qb, kb, kb};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(out, qb, ins[i], insz[i]) || overlaps(lse, lb, ins[i], insz[i]) ||
+            overlaps(workspace, ws_bytes, ins[i], insz[i]))
+            return ST_ERR_ALIAS;
+    if (overlaps(out, qb, lse, lb) || overlaps(workspace, ws_bytes, out, qb) ||
+        overlaps(workspace, ws_bytes, lse, lb))
+        return ST_ERR_ALIAS;
+    if (ws_bytes < st_attn3d_partial_workspace_bytes(T, H, W, n_text, heads, d, rope_split, dtype,
+                                                     kv_count))
+        return ST_ERR_WORKSPACE;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    char* ws = (char*)workspace;
+    float2* table = (float2*)ws;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dtype == ST_BF16) {
+        st::SeqLayout L;
+        L.n_segs = 1;
+        L.q_len = q_count;
+        L.kv_len = kv_count;
+        L.q_pos_base = q_begin;
+        L.kv_pos_base = kv_begin;
+        uint16_t* kt = (uint16_t*)(ws + table_bytes_for(T, H, W, rope_split));
+        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out, lse,
+                                        table, g, heads, L, stream);
+    } else {
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
+                                table, g, heads, d,
+                                f32_layout(1, q_count, 0, 1, kv_count, 0, 1, q_begin, kv_begin), stream);
+    }
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+st_status st_attn_merge(int n_parts, const void* const* o_parts, const float* const* lse_parts,
+                        int n_rows, int heads, int d, st_dtype dtype, void* out, float* lse_out,
+                        hipStream_t stream) {
+    if (!o_parts || !lse_parts || !out) return ST_ERR_NULL;
+    if (n_parts < 1 || n_parts > st::kMaxMergeParts) return ST_ERR_SHAPE;
+    if (n_rows < 1 || n_rows >= kMaxRows || heads < 1 || heads > 65535) return ST_ERR_SHAPE;
+    if ((long long)n_rows * heads >= (1LL << 31)) return ST_ERR_SHAPE;   // launch grid limit
+    if (dtype == ST_BF16) {
+        if (d < 8 || d % 8 || d > 512) return ST_ERR_UNSUPPORTED;
+    } else if (dtype == ST_F32) {
+        if (d < 4 || d % 4 || d > 256) return ST_ERR_UNSUPPORTED;
+    } else {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (!aligned(out, 16) || (lse_out && !aligned(lse_out, 4))) return ST_ERR_ALIGN;
+    const size_t ob = (size_t)n_rows * heads * d * elem_size(dtype);
+    const size_t lb = (size_t)n_rows * heads * sizeof(float);
+    for (int i = 0; i < n_parts; ++i) {
+        if (!o_parts[i] || !lse_parts[i]) return ST_ERR_NULL;
+        if (!aligned(o_parts[i], 16) || !aligned(lse_parts[i], 4)) return ST_ERR_ALIGN;
+        // Exact aliasing (in-place merge) is allowed; partial overlap is not.
+        if (out != o_parts[i] && overlaps(out, ob, o_parts[i], ob)) return ST_ERR_ALIAS;
+        if (lse_out && lse_out != lse_parts[i] && overlaps(lse_out, lb, lse_parts[i], lb))
+            return ST_ERR_ALIAS;
+        if (overlaps(out, ob, lse_parts[i], lb)) return ST_ERR_ALIAS;
+        if (lse_out && overlaps(lse_out, lb, o_parts[i], ob)) return ST_ERR_ALIAS;
+    }
+    if (lse_out && overlaps(out, ob, lse_out, lb)) return ST_ERR_ALIAS;
+    hipError_t e;
+    if (dtype == ST_BF16)
+        e = st::launch_merge_bf16(n_parts, (const uint16_t* const*)o_parts, lse_parts,
+                                  (long long)n_rows * heads, d, (uint16_t*)out, lse_out, stream);
+    else
+        e = st::launch_merge_f32(n_parts, (const float* const*)o_parts, lse_parts,
+                                 (long long)n_rows * heads, d, (float*)out, lse_out, stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 

@@ -108,22 +108,36 @@ hipError_t launch_rope_apply_bf16(const uint16_t* x, uint16_t* y, const RopeGeom
 hipError_t launch_rope_apply_f32(const float* x, float* y, const RopeGeom& g, int N, int heads,
                                  int d, const float2* table, hipStream_t stream);
 
-// Flash attention for bf16 storage, d = 128.  Sequences are contiguous row ranges
-// [s * seg_len, (s + 1) * seg_len) for s < n_segs: one segment of N rows for full attention,
-// T segments of H*W rows for the factorised spatial stage.
-//
+// Row layout of a batch of independent attention problems (per head).  Problem s reads query
+// buffer rows s * q_len .. and key/value buffer rows s * kv_len ..; RoPE positions are the buffer
+// row plus q_pos_base (queries) or kv_pos_base (keys), so a caller holding a run of a longer
+// sequence passes that run's first global row.  Full attention: one problem of N rows.
+// Factorised spatial stage: T problems of H*W rows.  Text cross-attention: one problem of
+// q_len video rows against kv_len text rows, with a geometry that rotates nothing.
+struct SeqLayout {
+    int n_segs;
+    int q_len;
+    int kv_len;
+    int q_pos_base;
+    int kv_pos_base;
+};
+
+// Flash attention for bf16 storage, d = 128.
 // Staged mode: launch_k_prep rotates K into fp16 tiles `kt` (attn_stage_elems(...) uint16
 // elements), then launch_attn_bf16_staged reads them together with V.
 // Fused mode: launch_attn_bf16_fused reads K directly and rotates it on every tile load.
-size_t attn_stage_elems(int heads, int seg_len, int n_segs);
+// `lse`, when not null, receives [q rows][heads] log-sum-exp of the scaled scores.
+size_t attn_stage_elems(int heads, int kv_len, int n_segs);
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
-                         int heads, int seg_len, int n_segs, hipStream_t stream);
+                         int heads, const SeqLayout& L, hipStream_t stream);
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
-                                   uint16_t* out, const float2* table, const RopeGeom& g,
-                                   int heads, int seg_len, int n_segs, hipStream_t stream);
+                                   uint16_t* out, float* lse, const float2* table,
+                                   const RopeGeom& g, int heads, const SeqLayout& L,
+                                   hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                  uint16_t* out, const float2* table, const RopeGeom& g,
-                                  int heads, int seg_len, int n_segs, hipStream_t stream);
+                                  uint16_t* out, float* lse, const float2* table,
+                                  const RopeGeom& g, int heads, const SeqLayout& L,
+                                  hipStream_t stream);
 
 // Factorised temporal stage, bf16, d = 128: for each spatial position s and head, the T rows
 // t * S + s attend to each other; values come from `vs` (the spatial stage's output).
@@ -131,10 +145,27 @@ hipError_t launch_attn_temporal_bf16(const uint16_t* q, const uint16_t* k, const
                                      const uint16_t* vs, uint16_t* out, const float2* table,
                                      const RopeGeom& g, int heads, hipStream_t stream);
 
-// fp32 checking kernel over row sets: sequence s holds rows s * base_mul + i * stride,
-// i < seq_len, for s < n_seqs.  Values from `v`, output rows written at the same indices.
-hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out,
+// fp32 checking kernel over row sets: problem s holds query buffer rows s * q_mul + i * q_stride
+// (i < q_len) and key/value buffer rows s * kv_mul + j * kv_stride (j < kv_len), for s < n_seqs;
+// positions are buffer rows plus the two position bases.  Output (and lse) rows are the query
+// buffer rows.
+struct F32Layout {
+    int n_seqs;
+    int q_len, q_mul, q_stride, q_pos_base;
+    int kv_len, kv_mul, kv_stride, kv_pos_base;
+};
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            const float2* table, const RopeGeom& g, int heads, int d,
-                           int n_seqs, int seq_len, int base_mul, int stride, hipStream_t stream);
+                           const F32Layout& L, hipStream_t stream);
+
+// Merge of partial results: out = sum_i exp(lse_i - lse) o_i, lse = log sum_i exp(lse_i), per
+// (row, head).  Up to kMaxMergeParts parts; out and lse_out may alias any part.
+constexpr int kMaxMergeParts = 16;
+hipError_t launch_merge_bf16(int n_parts, const uint16_t* const* o, const float* const* lse,
+                             long long rows_heads, int d, uint16_t* out, float* lse_out,
+                             hipStream_t stream);
+hipError_t launch_merge_f32(int n_parts, const float* const* o, const float* const* lse,
+                            long long rows_heads, int d, float* out, float* lse_out,
+                            hipStream_t stream);
 
 }  // namespace st

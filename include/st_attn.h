@@ -161,6 +161,52 @@ st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_tex
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Text cross-attention (the step after the self-attention in a Wan block: "04 · HunyuanVideo 与
+ * Wan", section 3.1; queries from the video tokens, keys and values from at most 512 text tokens,
+ * the text itself is not updated).  No rotation on either side; non-causal; scale 1/sqrt(d).
+ *   q, out  [n_q][heads][d];  k, v  [n_kv][heads][d];  out must not overlap q, k or v.
+ *   ST_BF16: d == 128, numerics as st_attn3d_fwd.  ST_F32: even d <= 128.
+ *   Workspace (caller-owned, 256-byte aligned): st_attn_cross_workspace_bytes bytes, holding an
+ *   identity table entry and, for bf16, the fp16 key tiles.
+ * ------------------------------------------------------------------------------------------- */
+size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dtype dtype);
+st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,
+                            int heads, int d, st_dtype dtype, void* workspace, size_t ws_bytes,
+                            void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Partial attention over a run of keys, and the merge of such partials (the single-device half
+ * of context parallelism: the CogVideoX record page, "Budget for that cost, because it grows",
+ * 2D ring and Ulysses; the first page's shard listing under "Position: RoPE in three
+ * dimensions": a device holds a contiguous run of tokens whose (t, h, w) are absolute).
+ *
+ * st_attn3d_partial_fwd: the rows of q are global rows [q_begin, q_begin + q_count) and the rows
+ * of k and v are global rows [kv_begin, kv_begin + kv_count) of the T*H*W + n_text sequence;
+ * every row is rotated by its own global position.  Writes
+ *   out [q_count][heads][d]  softmax over this run of keys times v (normalised, dtype of q)
+ *   lse [q_count][heads]     float32 log sum_j exp(q~ . k~_j / sqrt(d)) over the run (natural log)
+ * Workspace: st_attn3d_partial_workspace_bytes (0 for invalid arguments).  out, lse and the
+ * workspace must not overlap each other or any input.
+ *
+ * st_attn_merge: combines n_parts (1..16) partial results over disjoint runs of keys for the same
+ * query rows into the result over their union: lse = log sum_i exp(lse_i), out = sum_i
+ * exp(lse_i - lse) o_i, per (row, head).  o_parts and lse_parts are host arrays of device
+ * pointers ([n_rows][heads][d] and [n_rows][heads]); out may be exactly one of the o_parts and
+ * lse_out exactly one of the lse_parts (a running in-place merge); other overlaps are rejected.
+ * lse_out may be NULL.  ST_BF16 needs d % 8 == 0 (d <= 512), ST_F32 d % 4 == 0 (d <= 256).
+ * ------------------------------------------------------------------------------------------- */
+size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
+                                         const int rope_split[3], st_dtype dtype, int kv_count);
+st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                                int n_text, int heads, int d, const int rope_split[3], float theta,
+                                st_dtype dtype, int q_begin, int q_count, int kv_begin,
+                                int kv_count, void* workspace, size_t ws_bytes, void* out,
+                                float* lse, hipStream_t stream);
+st_status st_attn_merge(int n_parts, const void* const* o_parts, const float* const* lse_parts,
+                        int n_rows, int heads, int d, st_dtype dtype, void* out, float* lse_out,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Diagnostics.
  * ------------------------------------------------------------------------------------------- */
 

@@ -243,3 +243,90 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(72, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attn3d(x, x, x, (3, 4, 6))
+
+
+LSE = 0x600000000
+
+
+def test_cross_workspace_bytes(lib):
+    wb = lib.st_attn_cross_workspace_bytes(1000, 77, 3, 128, 0)
+    tiles = 3 * ((77 + 63) // 64) * 64 * 128 * 2
+    assert wb == 256 + ((tiles + 255) // 256) * 256
+    assert lib.st_attn_cross_workspace_bytes(1000, 77, 3, 64, 1) == 256
+    assert lib.st_attn_cross_workspace_bytes(1000, 77, 3, 64, 0) == 0      # bf16 needs d == 128
+    assert lib.st_attn_cross_workspace_bytes(0, 77, 3, 128, 0) == 0
+    assert lib.st_attn_cross_workspace_bytes(10, 0, 3, 128, 0) == 0
+
+
+def test_cross_rejects_invalid_arguments(lib):
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, n_q=1000, n_kv=77, heads=3, d=128, dtype=0, ws=WS, ws_bytes=1 << 24, out=OUT)
+        a.update(kw)
+        return lib.st_attn_cross_fwd(a["q"], a["k"], a["v"], a["n_q"], a["n_kv"], a["heads"], a["d"],
+                                     a["dtype"], a["ws"], a["ws_bytes"], a["out"], None)
+    assert f(q=None) == ST_ERR_NULL
+    assert f(ws=None) == ST_ERR_NULL
+    assert f(n_q=0) == ST_ERR_SHAPE
+    assert f(n_kv=0) == ST_ERR_SHAPE
+    assert f(n_kv=1 << 24) == ST_ERR_SHAPE
+    assert f(d=64) == ST_ERR_UNSUPPORTED
+    assert f(dtype=1, d=130) == ST_ERR_UNSUPPORTED
+    assert f(ws_bytes=1024) == ST_ERR_WORKSPACE
+    assert f(out=K + 512) == ST_ERR_ALIAS
+    assert f(ws=V) == ST_ERR_ALIAS
+    assert f(k=K + 8) == ST_ERR_ALIGN
+    assert f(ws=WS + 16) == ST_ERR_ALIGN
+
+
+def test_partial_workspace_bytes(lib):
+    table = lib.st_rope3d_table_bytes(3, 4, 6, sp(44, 42, 42))
+    tiles = 2 * ((30 + 63) // 64) * 64 * 128 * 2
+    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 30) == table + tiles
+    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 1, 30) == table
+    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 0) == 0
+    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 73) == 0
+
+
+def test_partial_rejects_invalid_arguments(lib):
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, T=3, H=4, W=6, n_text=5, heads=2, d=128, split=(44, 42, 42), theta=1e4,
+                 dtype=0, qb=10, qc=20, kb=40, kc=30, ws=WS, ws_bytes=1 << 24, out=OUT, lse=LSE)
+        a.update(kw)
+        return lib.st_attn3d_partial_fwd(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["n_text"],
+                                         a["heads"], a["d"], sp(*a["split"]), a["theta"], a["dtype"],
+                                         a["qb"], a["qc"], a["kb"], a["kc"], a["ws"], a["ws_bytes"],
+                                         a["out"], a["lse"], None)
+    assert f(lse=None) == ST_ERR_NULL
+    assert f(k=None) == ST_ERR_NULL
+    assert f(qb=-1) == ST_ERR_SHAPE
+    assert f(qc=0) == ST_ERR_SHAPE
+    assert f(qb=60, qc=18) == ST_ERR_SHAPE          # 60 + 18 > 72 + 5 rows
+    assert f(kb=50, kc=28) == ST_ERR_SHAPE
+    assert f(split=(44, 42, 40)) == ST_ERR_SPLIT
+    assert f(d=64, split=(20, 22, 22)) == ST_ERR_UNSUPPORTED
+    assert f(theta=0.0) == ST_ERR_UNSUPPORTED
+    assert f(ws_bytes=4096) == ST_ERR_WORKSPACE
+    assert f(lse=OUT + 256) == ST_ERR_ALIAS
+    assert f(out=V + 256) == ST_ERR_ALIAS
+    assert f(lse=LSE + 2) == ST_ERR_ALIGN
+
+
+def test_merge_rejects_invalid_arguments(lib):
+    import ctypes
+
+    def arr(*xs):
+        return (ctypes.c_void_p * len(xs))(*xs)
+
+    def f(n=2, o=(Q, K), l=(LSE, LSE + 0x10000), rows=100, heads=2, d=128, dtype=0, out=OUT, lse_out=WS):
+        return lib.st_attn_merge(n, arr(*o), arr(*l), rows, heads, d, dtype, out, lse_out, None)
+    assert f(out=None) == ST_ERR_NULL
+    assert f(o=(Q, None)) == ST_ERR_NULL
+    assert f(n=0) == ST_ERR_SHAPE
+    assert f(n=17, o=(Q,) * 17, l=(LSE,) * 17) == ST_ERR_SHAPE
+    assert f(rows=0) == ST_ERR_SHAPE
+    assert f(d=12) == ST_ERR_UNSUPPORTED
+    assert f(dtype=1, d=6) == ST_ERR_UNSUPPORTED
+    assert f(out=Q + 256) == ST_ERR_ALIAS            # partial overlap with a part
+    assert f(lse_out=LSE + 4) == ST_ERR_ALIAS
+    assert f(out=OUT + 8) == ST_ERR_ALIGN
+    assert f(o=(Q, K + 4)) == ST_ERR_ALIGN

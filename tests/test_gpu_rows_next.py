@@ -1,0 +1,140 @@
+"""GPU parity for the rows next to the hot path: text cross-attention, partial attention over a
+run of keys (with its log-sum-exp), and the merge of partials, against the float64 oracle.
+
+All calls go through the C ABI of libstattn.so.  Tolerances as in test_gpu_parity; the log-sum-exp
+of the bf16 path (scores from fp16-rounded rotated q and k) is checked to 1e-2 absolute, that of
+the fp32 mode to 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import full_spatiotemporal_attention_amd as fa
+from st_inputs import make_qkv, sample_rows
+from parity_util import assert_close, errors, host_f64, log, to_device
+
+pytestmark = pytest.mark.gpu
+
+WAN = (44, 42, 42)
+HUN = (16, 56, 56)
+LSE_TOL = {"bf16": 1e-2, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu_available():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    fa.library_path()
+
+
+def qkv_pair(n_q, n_kv, heads, dtype, seed):
+    """Queries from one seeded set, keys/values from another (different row counts)."""
+    xq = make_qkv(n_q, heads, 128, seed, dtype)
+    xk = make_qkv(n_kv, heads, 128, seed + 10, dtype)
+    q = to_device(xq)[0]
+    _, k, v = to_device(xk)
+    return xq.q, xk.k, xk.v, q, k, v
+
+
+# ---- text cross-attention -------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n_q,n_kv,heads", [(1000, 77, 3), (300, 512, 2), (1, 1, 1), (257, 64, 2),
+                                            (64, 129, 1)])
+def test_cross_attention(dtype, n_q, n_kv, heads):
+    log(f"  cross n_q={n_q} n_kv={n_kv} heads={heads} dtype={dtype} seed=7100")
+    qh, kh, vh, q, k, v = qkv_pair(n_q, n_kv, heads, dtype, 7100)
+    out = fa.attn_cross(q, k, v)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attention_ref(qh, kh, vh)
+    assert_close(host_f64(out), ref, dtype, f"cross {n_q}x{n_kv} {dtype}")
+
+
+def test_cross_attention_wan_text_sampled():
+    """Wan-shaped: 21x30x52 = 32,760 video queries against 512 text tokens, 12 heads."""
+    n_q, n_kv, heads = 32760, 512, 12
+    log(f"  cross n_q={n_q} n_kv={n_kv} heads={heads} dtype=bf16 seed=7200 rows=512")
+    qh, kh, vh, q, k, v = qkv_pair(n_q, n_kv, heads, "bf16", 7200)
+    out = fa.attn_cross(q, k, v)
+    torch.cuda.synchronize()
+    rows = sample_rows(n_q, n_q, 1560, 512, 7203)
+    ref = oracle.cross_attention_ref(qh, kh, vh, rows=rows)
+    assert_close(host_f64(out)[rows], ref, "bf16", "cross 32760x512 sampled")
+
+
+# ---- partial attention and merge ---------------------------------------------------------------
+
+def grid_inputs(grid, n_text, heads, dtype, seed, split):
+    n = grid[0] * grid[1] * grid[2] + n_text
+    x = make_qkv(n, heads, 128, seed, dtype)
+    return x, to_device(x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("grid,n_text,split,qb,qc,kb,kc", [
+    ((5, 6, 7), 9, WAN, 17, 100, 40, 90),
+    ((3, 8, 8), 0, HUN, 0, 192, 100, 92),
+    ((2, 5, 5), 4, WAN, 50, 4, 0, 1),
+])
+def test_partial_matches_oracle(dtype, grid, n_text, split, qb, qc, kb, kc):
+    log(f"  partial grid={grid} n_text={n_text} q=[{qb},+{qc}) kv=[{kb},+{kc}) dtype={dtype} seed=7300")
+    x, (q, k, v) = grid_inputs(grid, n_text, 2, dtype, 7300, split)
+    o, lse = fa.attn3d_partial(q[qb:qb + qc].contiguous(), k[kb:kb + kc].contiguous(),
+                               v[kb:kb + kc].contiguous(), grid, q_begin=qb, kv_begin=kb,
+                               n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    ro, rl = oracle.partial_attention_ref(x.q[qb:qb + qc], x.k[kb:kb + kc], x.v[kb:kb + kc], grid,
+                                          n_text, split, 10000.0, q_begin=qb, kv_begin=kb)
+    assert_close(host_f64(o), ro, dtype, f"partial o {dtype}")
+    err = float(np.abs(host_f64(lse) - rl).max())
+    log(f"    partial lse max_abs={err:.3e}")
+    assert err <= LSE_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_of_key_runs_equals_full_attention(dtype):
+    grid, n_text, split, heads = (4, 9, 10), 20, WAN, 2
+    n = grid[0] * grid[1] * grid[2] + n_text
+    cuts = [0, 100, 101, 230, n]
+    log(f"  merge grid={grid} n_text={n_text} runs={cuts} dtype={dtype} seed=7400")
+    x, (q, k, v) = grid_inputs(grid, n_text, heads, dtype, 7400, split)
+    parts = [fa.attn3d_partial(q, k[a:b].contiguous(), v[a:b].contiguous(), grid, q_begin=0,
+                               kv_begin=a, n_text=n_text, rope_split=split)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = fa.attn_merge(parts)
+    torch.cuda.synchronize()
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, grid, n_text, split, 10000.0)
+    assert_close(host_f64(o), ref, dtype, f"merge of 4 runs {dtype}")
+    _, rl = oracle.partial_attention_ref(x.q, x.k, x.v, grid, n_text, split)
+    err = float(np.abs(host_f64(lse) - rl).max())
+    log(f"    merged lse max_abs={err:.3e}")
+    assert err <= LSE_TOL[dtype]
+    # the merge kernel alone, on the GPU's own partials, against the oracle's merge of them
+    ro, rl2 = oracle.merge_partials_ref([(host_f64(a), host_f64(b)) for a, b in parts])
+    m_abs, m_rel = errors(host_f64(o), ro)
+    log(f"    merge kernel vs oracle merge of the same partials: max_abs={m_abs:.3e} rel_l2={m_rel:.3e}")
+    if dtype == "f32":
+        assert m_abs <= 1e-6
+    else:
+        assert m_abs <= 2 ** -8 * float(np.abs(ro).max()) + 1e-6   # one bf16 rounding of the output
+    assert float(np.abs(host_f64(lse) - rl2).max()) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_in_place_and_single_part(dtype):
+    grid, split, heads = (3, 6, 6), WAN, 3
+    n = grid[0] * grid[1] * grid[2]
+    log(f"  merge in place grid={grid} dtype={dtype} seed=7500")
+    x, (q, k, v) = grid_inputs(grid, 0, heads, dtype, 7500, split)
+    parts = [fa.attn3d_partial(q, k[a:b].contiguous(), v[a:b].contiguous(), grid, kv_begin=a,
+                               rope_split=split) for a, b in [(0, 40), (40, n)]]
+    o_ref, l_ref = fa.attn_merge(parts)
+    o0, l0 = parts[0][0].clone(), parts[0][1].clone()
+    o_one, l_one = fa.attn_merge([(o0, l0)])
+    o_in, l_in = fa.attn_merge(parts, out=parts[0][0], lse_out=parts[0][1])
+    torch.cuda.synchronize()
+    assert o_in.data_ptr() == parts[0][0].data_ptr()
+    assert torch.equal(o_in, o_ref) and torch.equal(l_in, l_ref)
+    assert float((o_one.float() - o0.float()).abs().max()) <= (2 ** -8 if dtype == "bf16" else 1e-6)
+    assert float((l_one - l0).abs().max()) <= 1e-6
