@@ -17,6 +17,7 @@ from .st_oracle import (  # noqa: F401
     metric_flops,
     factorized_flops,
     partial_attention_ref,
+    qkv_rope_ref,
     rope_frequencies,
     rope_pair_layout,
     rope3d_ref,

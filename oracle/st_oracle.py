@@ -27,6 +27,10 @@ What it computes, and where each step comes from (page title, then section):
 * Text cross-attention -- "04 · HunyuanVideo 与 Wan", section 3.1 (one Wan block step by step):
   queries come from the video tokens, keys and values from the text condition (at most 512
   tokens, same section), and the text is not updated by this step.
+* QKV projection with the 3D rotation applied to its output -- "04 · HunyuanVideo 与 Wan", section
+  3.1 (the Wan block's projections Q = X W_Q, K = X W_K, V = X W_V) and the first page's cost
+  model (the linear layers, 24 N D^2 per layer, of which the QKV projection is 6 N D^2); the
+  rotation is the same 3D RoPE of q and k, applied to the projection's output.
 * Partial attention and its merge -- the CogVideoX record page ("Budget for that cost, because it
   grows": attention is split across devices by context parallelism, 2D ring and Ulysses) and the
   first page's shard listing under "Position: RoPE in three dimensions" (each device holds a
@@ -76,6 +80,7 @@ __all__ = [
     "cross_attention_ref",
     "partial_attention_ref",
     "merge_partials_ref",
+    "qkv_rope_ref",
 ]
 
 
@@ -373,3 +378,34 @@ def merge_partials_ref(parts):
     lse = m + np.log(tot)
     o = sum((w[i] / tot)[:, :, None] * np.asarray(parts[i][0], ORACLE_DTYPE) for i in range(len(parts)))
     return o, lse
+
+
+def qkv_rope_ref(x, w, bias, grid, n_text: int = 0, split=(44, 42, 42), theta: float = 10000.0,
+                 heads: int = None, rows=None):
+    """QKV projection of x with the 3D rotation of q and k: returns (q~, k~, v), each [rows, heads, d].
+
+    x [N, C], w [3C, C] (output features by input features, rows 0..C-1 give q, C..2C-1 give k,
+    2C..3C-1 give v; feature f of a third is channel f % d of head f // d), bias [3C] or None.
+    y = x w^T + bias in float64; q and k are then rotated by each row's (t, h, w).
+    """
+    x = np.asarray(x, ORACLE_DTYPE)
+    w = np.asarray(w, ORACLE_DTYPE)
+    n, c = x.shape
+    if w.shape != (3 * c, c):
+        raise ValueError("w must be [3C, C]")
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows)
+    d = sum(split)
+    if heads is None:
+        heads = c // d
+    if heads * d != c:
+        raise ValueError("C must be heads * d")
+    y = x[rows] @ w.T
+    if bias is not None:
+        y = y + np.asarray(bias, ORACLE_DTYPE)[None, :]
+    q = y[:, :c].reshape(rows.size, heads, d)
+    k = y[:, c:2 * c].reshape(rows.size, heads, d)
+    v = y[:, 2 * c:].reshape(rows.size, heads, d)
+    return (rope3d_ref(q, grid, n_text, split, theta, rows=rows),
+            rope3d_ref(k, grid, n_text, split, theta, rows=rows), v)

@@ -640,3 +640,77 @@ def test_planted_merge_mistakes_are_caught(mode):
     qr = oracle.rope3d_ref(q, grid, n_text, split)
     kr = oracle.rope3d_ref(k, grid, n_text, split)
     assert np.abs(o - _sdpa64(qr, kr, v)).max() > 1e-3
+
+
+# ---- QKV projection with the rotation of its output ---------------------------------------------
+
+def test_qkv_projection_matches_explicit_sums():
+    """The product part against plain nested sums (no matrix routine); with T' = 1 and the whole
+    head in the t range every row sits at t = 0, so nothing is rotated."""
+    rng = np.random.default_rng(81)
+    grid, heads, d = (1, 2, 2), 2, 4
+    n, c = 4, heads * d
+    x = rng.standard_normal((n, c))
+    w = rng.standard_normal((3 * c, c))
+    b = rng.standard_normal(3 * c)
+    q, k, v = oracle.qkv_rope_ref(x, w, b, grid, 0, (4, 0, 0))
+    for r in range(n):
+        for f in range(3 * c):
+            acc = b[f]
+            for i in range(c):
+                acc += x[r, i] * w[f, i]
+            sec, rem = divmod(f, c)
+            got = (q, k, v)[sec][r, rem // d, rem % d]
+            assert abs(got - acc) < 1e-12
+
+
+def test_qkv_rope_rotates_q_and_k_only_and_bias_passes_through():
+    rng = np.random.default_rng(82)
+    grid, split, heads = (2, 2, 3), (4, 2, 2), 2
+    c = heads * 8
+    n = 12
+    x = rng.standard_normal((n, c))
+    w = np.zeros((3 * c, c))
+    b = rng.standard_normal(3 * c)
+    q, k, v = oracle.qkv_rope_ref(x, w, b, grid, 0, split)
+    bq = np.broadcast_to(b[:c].reshape(1, heads, 8), (n, heads, 8))
+    np.testing.assert_allclose(q, oracle.rope3d_ref(bq, grid, 0, split), atol=1e-14)
+    np.testing.assert_allclose(v, np.broadcast_to(b[2 * c:].reshape(1, heads, 8), (n, heads, 8)), atol=0)
+    # row 0 sits at the origin: no rotation there
+    np.testing.assert_allclose(k[0], b[c:2 * c].reshape(heads, 8), atol=1e-15)
+
+
+def test_qkv_rope_then_plain_attention_equals_full_attention():
+    """Projection + rotation, then attention without rotation == full 3D-RoPE attention of x W."""
+    rng = np.random.default_rng(83)
+    grid, n_text, split, heads, d = (2, 3, 2), 3, (4, 2, 2), 2, 8
+    c = heads * d
+    n = grid[0] * grid[1] * grid[2] + n_text
+    x = rng.standard_normal((n, c))
+    w = rng.standard_normal((3 * c, c)) / np.sqrt(c)
+    q, k, v = oracle.qkv_rope_ref(x, w, None, grid, n_text, split)
+    got = oracle.cross_attention_ref(q, k, v)
+    y = x @ w.T
+    ref = oracle.full_attention_ref(y[:, :c].reshape(n, heads, d), y[:, c:2 * c].reshape(n, heads, d),
+                                    y[:, 2 * c:].reshape(n, heads, d), grid, n_text, split)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([1, 7, n - 1])
+    qs, ks, vs = oracle.qkv_rope_ref(x, w, None, grid, n_text, split, rows=rows)
+    np.testing.assert_allclose(qs, q[rows], atol=0)
+    np.testing.assert_allclose(vs, v[rows], atol=0)
+
+
+@pytest.mark.parametrize("mode", ["w_not_transposed", "sections_swapped"])
+def test_planted_qkv_mistakes_are_caught(mode):
+    rng = np.random.default_rng(84)
+    grid, split, heads, d = (1, 2, 2), (4, 0, 0), 1, 4
+    c = heads * d
+    x = rng.standard_normal((4, c))
+    w = rng.standard_normal((3 * c, c))
+    q, k, v = oracle.qkv_rope_ref(x, w, None, grid, 0, split)
+    if mode == "w_not_transposed":
+        y = x @ w[:c]
+        assert np.abs(y.reshape(4, heads, d) - q).max() > 1e-3
+    else:
+        y = x @ w[c:2 * c].T
+        assert np.abs(y.reshape(4, heads, d) - q).max() > 1e-3
