@@ -303,6 +303,24 @@ def main():
         merge_bytes = 3.0 * q.numel() * 2 + 3.0 * n * HEADS * 4
         extras["merge2_ms"] = round(merge_ms, 4)
         extras["merge2_GBps"] = round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)
+        # QKV projection with the rotation of q and k in its epilogue (Wan2.1-1.3B: C = 1536).
+        C = HEADS * D
+        gx = torch.Generator(device=dev).manual_seed(SEED + 30)
+        xq = torch.randn(n, C, device=dev, generator=gx).to(torch.bfloat16)
+        wq = (torch.randn(3 * C, C, device=dev, generator=gx) / C ** 0.5).to(torch.bfloat16)
+        bq = (0.1 * torch.randn(3 * C, device=dev, generator=gx)).to(torch.bfloat16)
+        qws = torch.empty(max(256, fa.rope3d_table_bytes(GRID, SPLIT)), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            fa.qkv_rope(xq, wq, GRID, bias=bq, rope_split=SPLIT, workspace=qws)
+        e0.record(stream)
+        for _ in range(reps):
+            fa.qkv_rope(xq, wq, GRID, bias=bq, rope_split=SPLIT, workspace=qws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qkv_ms = e0.elapsed_time(e1) / reps
+        extras["qkv_rope_ms"] = round(qkv_ms, 4)
+        extras["qkv_rope_TFLOPs"] = round(2.0 * n * C * 3 * C / (qkv_ms * 1e-3) / 1e12, 2)
+        del xq, wq, bq
         result["extras"] = extras
         eprint(f"extras: {extras}")
 

@@ -22,6 +22,7 @@ __all__ = [
     "attn_cross",
     "attn3d_partial",
     "attn_merge",
+    "qkv_rope",
     "rope3d_apply",
     "rope3d_table",
     "attn3d_workspace_bytes",
@@ -296,3 +297,36 @@ def attn_merge(parts, out=None, lse_out=None):
                            lse_out.data_ptr(), _stream(o0.device))
     _lib.check("st_attn_merge", st)
     return out, lse_out
+
+
+def qkv_rope(x, w, grid, bias=None, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, workspace=None):
+    """QKV projection x w^T (+ bias) with q and k rotated by 3D RoPE; returns (q, k, v) [N, heads, d].
+
+    x [N, C], w [3C, C] (a linear layer's weight), bias [3C] or None; C = heads * d with d the
+    sum of rope_split.
+    """
+    lib = _lib.load()
+    T, H, W = (int(a) for a in grid)
+    d = int(sum(rope_split))
+    for t in (x, w) + ((bias,) if bias is not None else ()):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("expected contiguous GPU tensors")
+        if t.dtype != x.dtype:
+            raise ValueError("x, w and bias must share a dtype")
+    n, c = x.shape
+    if w.shape != (3 * c, c) or c % d:
+        raise ValueError("w must be [3C, C] and C a multiple of the head dim")
+    heads = c // d
+    code = _dtype_code(x)
+    q = torch.empty((n, heads, d), dtype=x.dtype, device=x.device)
+    k = torch.empty_like(q)
+    v = torch.empty_like(q)
+    sp = _lib.split_arg(rope_split)
+    nbytes = int(lib.st_qkv_rope_workspace_bytes(T, H, W, sp))
+    ws = _workspace(nbytes, x.device, workspace)
+    st = lib.st_qkv_rope_fwd(x.data_ptr(), w.data_ptr(), None if bias is None else bias.data_ptr(),
+                             T, H, W, int(n_text), heads, d, sp, float(theta), code, ws.data_ptr(),
+                             ws.numel() * ws.element_size(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             _stream(x.device))
+    _lib.check("st_qkv_rope_fwd", st)
+    return q, k, v

@@ -41,6 +41,8 @@ SIGNATURES = {
     "st_attn3d_partial_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _i, _i, _i, _i,
                                    _p, _sz, _p, _p, _p]),
     "st_attn_merge": (_i, [_i, ctypes.POINTER(_p), ctypes.POINTER(_p), _i, _i, _i, _i, _p, _p, _p]),
+    "st_qkv_rope_workspace_bytes": (_sz, [_i, _i, _i, _split]),
+    "st_qkv_rope_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p, _p, _p]),
     "st_status_str": (ctypes.c_char_p, [_i]),
     "st_last_hip_error": (_i, []),
     "st_version": (ctypes.c_char_p, []),

@@ -20,7 +20,8 @@ LIB_NAME = "libstattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["st_api.hip", "rope.hip", "attn_bf16.hip", "attn_temporal.hip", "attn_f32.hip", "merge.hip"]
+SOURCES = ["st_api.hip", "rope.hip", "attn_bf16.hip", "attn_temporal.hip", "attn_f32.hip", "merge.hip",
+           "qkv_rope.hip"]
 
 # Extra flags per source.  The flash kernels take row maxima of MFMA results with fmaxf; without
 # -fno-honor-nans every operand is first canonicalised (an extra v_max_f32 x, x each).  A NaN

@@ -1,0 +1,329 @@
+// QKV projection with the 3D rotation fused into its epilogue.
+//
+// The step before the attention in a video DiT block ("04 · HunyuanVideo 与 Wan", section 3.1:
+// Q = X W_Q, K = X W_K, V = X W_V; the first page's cost model counts it in the linear layers):
+// y = x W^T + bias for x [N][C] and W [3C][C] (output features by input features, the usual
+// layout of a linear layer's weight), then q and k are turned by each row's 3D RoPE ("A video
+// model's architecture", "Position: RoPE in three dimensions") before they are stored.  Writing
+// rotated q and k once here leaves the attention nothing to rotate.
+//
+// bf16 kernel (MFMA): one workgroup of 8 waves computes a 256-token x 256-feature tile of y^T
+// (features as rows, so that each lane holds 4 consecutive features of one token: a RoPE pair is
+// in-lane).  Wave w takes features 64 (w % 4) .. +63 and tokens 128 (w / 4) .. +127: 2 x 4 blocks
+// of 32 x 32.  K advances 64 at a time through two LDS stages (x tile and W tile, 32 KB each),
+// copied by LDS DMA one stage ahead of the MFMAs.  The output tile goes through LDS so that rows
+// are written whole.
+#include "st_internal.h"
+
+namespace st {
+namespace {
+
+constexpr int GM = 256;                     // tokens per tile
+constexpr int GN = 256;                     // output features per tile
+constexpr int GK = 64;                      // input features per stage
+constexpr int G_TILE = GM * GK * 2;         // 32 KB: one x or W tile of a stage
+constexpr int G_STAGE = 2 * G_TILE;         // x tile, then W tile
+constexpr int G_LDS = 2 * G_STAGE;          // two stages; the output tile reuses all of it
+constexpr int GTHREADS = 512;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+struct QkvParams {
+    const uint16_t* x;
+    const uint16_t* w;
+    const uint16_t* bias;   // [3C] or null
+    uint16_t* q;
+    uint16_t* k;
+    uint16_t* v;
+    const float2* table;
+    RopeGeom g;
+    int n_rows;
+    int C;
+    int m_tiles;
+    int n_tiles;
+    int total_wg;
+};
+
+// 16-byte chunk c of a 128-byte tile row r sits at physical chunk c ^ ((r >> 1) & 7): the 16
+// lanes of a 16-byte read (16 consecutive rows, one chunk) then cover all 64 banks.
+__device__ __forceinline__ int g_swz(int r) { return (r >> 1) & 7; }
+
+__global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[G_LDS];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
+
+    const int logical = xcd_remap(blockIdx.x, p.total_wg);
+    const int mt = logical / p.n_tiles;
+    const int nt = logical - mt * p.n_tiles;
+    const int m0 = mt * GM;                  // first token
+    const int f0 = nt * GN;                  // first output feature
+    const int C = p.C;
+    const int F = 3 * C;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+    const int fg = wave & 3;
+    const int tg = wave >> 2;
+
+    // ---- stage copies: wave w copies rows 32 w .. +31 of the x tile and of the W tile --------
+    uint32_t x_off[4], w_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 32 * wave + 8 * i + (lane >> 3);
+        const int c = (lane & 7) ^ g_swz(r);
+        const int tr = min(m0 + r, p.n_rows - 1);      // rows past the end repeat the last row
+        const int fr = min(f0 + r, F - 1);
+        x_off[i] = 2u * (uint32_t)(tr * C + 8 * c);
+        w_off[i] = 2u * (uint32_t)(fr * C + 8 * c);
+    }
+    auto issue_stage = [&](int ks, int stage) {
+        const uint16_t* xb = p.x + ks * GK;
+        const uint16_t* wb = p.w + ks * GK;
+        const uint32_t sb = lds0 + stage * G_STAGE + (32 * wave) * 128;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(xb, x_off[i], sb + i * 1024);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(wb, w_off[i], sb + G_TILE + i * 1024);
+    };
+
+    // ---- operand reads -------------------------------------------------------------------------
+    // A (W rows = features) for feature block fb, B (x rows = tokens) for token block tb, k16
+    // step kk: row l32 of the block, logical chunk 2 kk + hh.
+    uint32_t a_rd[2], b_rd[4];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb) a_rd[fb] = lds0 + G_TILE + (64 * fg + 32 * fb + l32) * 128;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) b_rd[tb] = lds0 + (128 * tg + 32 * tb + l32) * 128;
+    const int rsw = g_swz(l32);   // rows of a block start at multiples of 32: same swizzle
+    auto rd = [&](uint32_t base, int stage, int kk) -> bf16x8_t {
+        const uint32_t a = base + stage * G_STAGE + 16 * ((2 * kk + hh) ^ rsw);
+        return *(__attribute__((address_space(3))) const bf16x8_t*)(uintptr_t)a;
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[fb][tb][i] = 0.0f;
+
+    const int ksteps = C / GK;
+    issue_stage(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    auto step = [&](auto stc, int ks) {
+        constexpr int st = decltype(stc)::value;
+        if (ks + 1 < ksteps) issue_stage(ks + 1, st ^ 1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            bf16x8_t a[2], b[4];
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb) a[fb] = rd(a_rd[fb], st, kk);
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) b[tb] = rd(b_rd[tb], st, kk);
+#pragma unroll
+            for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fb], b[tb], acc[fb][tb], 0, 0, 0);
+            // Keep the operand reads of one k16 step next to its MFMAs (register use).
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    // C is a multiple of 128 (heads x 128), so the k steps come in pairs.
+    for (int ks = 0; ks < ksteps; ks += 2) {
+        step(std::integral_constant<int, 0>{}, ks);
+        step(std::integral_constant<int, 1>{}, ks + 1);
+    }
+
+    // ---- epilogue: bias, rotation of q and k, bf16, through LDS to whole rows ------------------
+    // Lane (l32, hh) holds, for block (fb, tb), token 128 tg + 32 tb + l32 and features
+    // 64 fg + 32 fb + 8 (i / 4) + 4 hh + i % 4 of the tile.
+    const RopeGeom& g = p.g;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+        __builtin_amdgcn_sched_barrier(0);            // one token block at a time (register use)
+        const int row = 128 * tg + 32 * tb + l32;     // token row inside the tile
+        const int n = min(m0 + row, p.n_rows - 1);
+        int t = 0, h = 0, w = 0;
+        const bool text = n >= g.Nv;
+        if (!text) decode_pos(n, g, t, h, w);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int fl = 64 * fg + 32 * fb + 8 * gi + 4 * hh;   // first of 4 features, in tile
+                const int f = f0 + fl;
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][4 * gi + e];
+                if (p.bias && f < F) {
+                    const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + f);
+                    y[0] += bf16_lo(bw.x);
+                    y[1] += bf16_hi(bw.x);
+                    y[2] += bf16_lo(bw.y);
+                    y[3] += bf16_hi(bw.y);
+                }
+                if (f < 2 * C) {                  // q or k: rotate pairs (f, f+1), (f+2, f+3)
+                    const int pair = (f % 128) >> 1;
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float2 cs = p.table[pair_entry(pair + e, t, h, w, text, g)];
+                        rotate_pair(y[2 * e], y[2 * e + 1], cs);
+                    }
+                }
+                const u32x2_t pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                const uint32_t a = lds0 + row * 512 + 16 * ((fl >> 3) ^ (row & 31)) + 8 * hh;
+                *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)a = pk;
+            }
+    }
+    __syncthreads();
+    // Wave w writes tile rows 32 w .. +31, two rows (2 x 512 bytes) per store.
+#pragma unroll 4
+    for (int i = 0; i < 16; ++i) {
+        const int row = 32 * wave + 2 * i + (lane >> 5);
+        const int c = lane & 31;                       // logical 16-byte chunk: features 8c .. 8c+7
+        const u32x4_t val = *(__attribute__((address_space(3))) const u32x4_t*)(uintptr_t)(
+            lds0 + row * 512 + 16 * (c ^ (row & 31)));
+        const int n = m0 + row;
+        const int f = f0 + 8 * c;
+        if (n < p.n_rows && f < F) {
+            const int sec = f / C;
+            uint16_t* dst = (sec == 0 ? p.q : (sec == 1 ? p.k : p.v)) + (long long)n * C + (f - sec * C);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(val[0], val[1], val[2], val[3]);
+        }
+    }
+}
+
+// ---- float32 checking kernel: 64 x 64 output tiles, 4 x 4 per thread ---------------------------
+struct QkvF32Params {
+    const float* x;
+    const float* w;
+    const float* bias;
+    float* q;
+    float* k;
+    float* v;
+    const float2* table;
+    RopeGeom g;
+    int n_rows;
+    int C;
+    int d;
+};
+
+__global__ void __launch_bounds__(256) qkv_rope_f32_kernel(QkvF32Params p) {
+    __shared__ float xs[16][64 + 1];
+    __shared__ float ws[16][64 + 1];
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int m0 = blockIdx.y * 64, f0 = blockIdx.x * 64;
+    const int C = p.C, F = 3 * C;
+    float acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = 0.0f;
+    for (int k0 = 0; k0 < C; k0 += 16) {
+        for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+            const int r = idx >> 4, kk = idx & 15;
+            const int n = m0 + r, f = f0 + r, kc = k0 + kk;
+            xs[kk][r] = (n < p.n_rows && kc < C) ? p.x[(long long)n * C + kc] : 0.0f;
+            ws[kk][r] = (f < F && kc < C) ? p.w[(long long)f * C + kc] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(xs[kk][4 * ty + a], ws[kk][4 * tx + b], acc[a][b]);
+        __syncthreads();
+    }
+    const RopeGeom& g = p.g;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int n = m0 + 4 * ty + a;
+        if (n >= p.n_rows) continue;
+        int t = 0, h = 0, w = 0;
+        const bool text = n >= g.Nv;
+        if (!text) decode_pos(n, g, t, h, w);
+        float y[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int f = f0 + 4 * tx + b;
+            y[b] = acc[a][b] + ((p.bias && f < F) ? p.bias[f] : 0.0f);
+        }
+        const int fb = f0 + 4 * tx;               // 4 features, fb even: pairs (fb, fb+1), (fb+2, fb+3)
+        if (fb < 2 * C) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int f = fb + 2 * e;
+                const int pair = (f % p.d) >> 1;
+                rotate_pair(y[2 * e], y[2 * e + 1], p.table[pair_entry(pair, t, h, w, text, g)]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int f = fb + b;
+            if (f >= F) continue;
+            const int sec = f / C;
+            float* dst = sec == 0 ? p.q : (sec == 1 ? p.k : p.v);
+            dst[(long long)n * C + (f - sec * C)] = y[b];
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_qkv_rope_bf16(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
+                                uint16_t* q, uint16_t* k, uint16_t* v, const float2* table,
+                                const RopeGeom& g, int n_rows, int C, hipStream_t stream) {
+    QkvParams p;
+    p.x = x;
+    p.w = w;
+    p.bias = bias;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.table = table;
+    p.g = g;
+    p.n_rows = n_rows;
+    p.C = C;
+    p.m_tiles = (n_rows + GM - 1) / GM;
+    p.n_tiles = (3 * C + GN - 1) / GN;
+    p.total_wg = p.m_tiles * p.n_tiles;
+    hipLaunchKernelGGL(qkv_rope_bf16_kernel, dim3(p.total_wg), dim3(GTHREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope_f32(const float* x, const float* w, const float* bias, float* q, float* k,
+                               float* v, const float2* table, const RopeGeom& g, int n_rows, int C,
+                               int d, hipStream_t stream) {
+    QkvF32Params p;
+    p.x = x;
+    p.w = w;
+    p.bias = bias;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.table = table;
+    p.g = g;
+    p.n_rows = n_rows;
+    p.C = C;
+    p.d = d;
+    dim3 grid((3 * C + 63) / 64, (n_rows + 63) / 64);
+    hipLaunchKernelGGL(qkv_rope_f32_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace st

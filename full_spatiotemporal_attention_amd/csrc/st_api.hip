@@ -462,6 +462,67 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
+// ---- QKV projection with the rotation of q and k ------------------------------------------------
+
+size_t st_qkv_rope_workspace_bytes(int T, int H, int W, const int rope_split[3]) {
+    return st_rope3d_table_bytes(T, H, W, rope_split);
+}
+
+st_status st_qkv_rope_fwd(const void* x, const void* w, const void* bias, int T, int H, int W,
+                          int n_text, int heads, int d, const int rope_split[3], float theta,
+                          st_dtype dtype, void* workspace, size_t ws_bytes, void* q, void* k,
+                          void* v, hipStream_t stream) {
+    if (!x || !w || !q || !k || !v || !workspace || !rope_split) return ST_ERR_NULL;
+    long long n = 0;
+    if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
+    if (heads < 1 || heads > 65535 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
+    st_status s = check_split(rope_split, d);
+    if (s != ST_OK) return s;
+    const long long C = (long long)heads * d;
+    if (dtype == ST_BF16) {
+        if (d != 128) return ST_ERR_UNSUPPORTED;
+        // 32-bit byte offsets inside the kernel
+        if (n * C * 2 >= (1LL << 31) || 3 * C * C * 2 >= (1LL << 31)) return ST_ERR_SHAPE;
+    } else if (dtype == ST_F32) {
+        if (d > 128) return ST_ERR_UNSUPPORTED;
+        if (n * C >= (1LL << 40)) return ST_ERR_SHAPE;
+    } else {
+        return ST_ERR_UNSUPPORTED;
+    }
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+        (bias && !aligned(bias, 8)))
+        return ST_ERR_ALIGN;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    if (ws_bytes < st_qkv_rope_workspace_bytes(T, H, W, rope_split)) return ST_ERR_WORKSPACE;
+    const size_t es = elem_size(dtype);
+    const size_t xb = (size_t)(n * C) * es, wb = (size_t)(3 * C * C) * es, bb = (size_t)(3 * C) * es;
+    const void* ins[3] = {x, w, bias};
+    const size_t insz[3] = {xb, wb, bb};
+    void* outs[3] = {q, k, v};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 3; ++i)
+            if (ins[i] && overlaps(outs[o], xb, ins[i], insz[i])) return ST_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 3; ++o2)
+            if (overlaps(outs[o], xb, outs[o2], xb)) return ST_ERR_ALIAS;
+        if (overlaps(workspace, ws_bytes, outs[o], xb)) return ST_ERR_ALIAS;
+    }
+    for (int i = 0; i < 3; ++i)
+        if (ins[i] && overlaps(workspace, ws_bytes, ins[i], insz[i])) return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    float2* table = (float2*)workspace;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dtype == ST_BF16)
+        e = st::launch_qkv_rope_bf16((const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias,
+                                     (uint16_t*)q, (uint16_t*)k, (uint16_t*)v, table, g, (int)n,
+                                     (int)C, stream);
+    else
+        e = st::launch_qkv_rope_f32((const float*)x, (const float*)w, (const float*)bias, (float*)q,
+                                    (float*)k, (float*)v, table, g, (int)n, (int)C, d, stream);
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
 // ---- partial attention over a run of keys, and the merge -----------------------------------------
 
 size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,

@@ -158,6 +158,15 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float
                            const float2* table, const RopeGeom& g, int heads, int d,
                            const F32Layout& L, hipStream_t stream);
 
+// QKV projection x [n_rows][C] times w^T (w [3C][C]) plus bias, q and k rotated, written to
+// q, k, v [n_rows][C].  bf16 needs C % 64 == 0 and d == 128; the f32 kernel takes any even d.
+hipError_t launch_qkv_rope_bf16(const uint16_t* x, const uint16_t* w, const uint16_t* bias,
+                                uint16_t* q, uint16_t* k, uint16_t* v, const float2* table,
+                                const RopeGeom& g, int n_rows, int C, hipStream_t stream);
+hipError_t launch_qkv_rope_f32(const float* x, const float* w, const float* bias, float* q, float* k,
+                               float* v, const float2* table, const RopeGeom& g, int n_rows, int C,
+                               int d, hipStream_t stream);
+
 // Merge of partial results: out = sum_i exp(lse_i - lse) o_i, lse = log sum_i exp(lse_i), per
 // (row, head).  Up to kMaxMergeParts parts; out and lse_out may alias any part.
 constexpr int kMaxMergeParts = 16;

@@ -175,6 +175,27 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
                             void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * QKV projection with the 3D rotation of its q and k outputs (the projections before the
+ * attention of a Wan block: "04 · HunyuanVideo 与 Wan", section 3.1; the rotation as in
+ * st_attn3d_fwd, "A video model's architecture", "Position: RoPE in three dimensions").
+ *   x     [N][C] with N = T*H*W + n_text rows and C = heads * d input features
+ *   w     [3C][C] output features by input features (a linear layer's weight layout); output
+ *         feature f < C is q channel f % d of head f / d, C <= f < 2C is k, the rest v
+ *   bias  [3C] or NULL
+ *   q, k, v  [N][heads][d]: q = R(x w_q^T + b_q), k = R(x w_k^T + b_k), v = x w_v^T + b_v, where R
+ *         turns each row by its (t, h, w) (text rows unchanged)
+ * ST_BF16: d == 128; products on bf16 MFMA with fp32 accumulation, bias and rotation in fp32,
+ * results rounded once to bf16; N*C*2 and 3C*C*2 bytes each below 2^31.  ST_F32: even d <= 128,
+ * fp32 throughout.  Outputs must not overlap each other or the inputs.  Workspace (256-byte
+ * aligned): st_qkv_rope_workspace_bytes bytes (the angle table).
+ * ------------------------------------------------------------------------------------------- */
+size_t st_qkv_rope_workspace_bytes(int T, int H, int W, const int rope_split[3]);
+st_status st_qkv_rope_fwd(const void* x, const void* w, const void* bias, int T, int H, int W,
+                          int n_text, int heads, int d, const int rope_split[3], float theta,
+                          st_dtype dtype, void* workspace, size_t ws_bytes, void* q, void* k,
+                          void* v, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Partial attention over a run of keys, and the merge of such partials (the single-device half
  * of context parallelism: the CogVideoX record page, "Budget for that cost, because it grows",
  * 2D ring and Ulysses; the first page's shard listing under "Position: RoPE in three

@@ -330,3 +330,28 @@ def test_merge_rejects_invalid_arguments(lib):
     assert f(lse_out=LSE + 4) == ST_ERR_ALIAS
     assert f(out=OUT + 8) == ST_ERR_ALIGN
     assert f(o=(Q, K + 4)) == ST_ERR_ALIGN
+
+
+def test_qkv_rope_rejects_invalid_arguments(lib):
+    Wt, Kt, Vt, B = 0x700000000, 0x800000000, 0x900000000, 0xA00000000
+
+    def f(**kw):
+        a = dict(x=Q, w=Wt, b=B, T=3, H=4, W=6, n_text=2, heads=2, d=128, split=(44, 42, 42), theta=1e4,
+                 dtype=0, ws=WS, ws_bytes=1 << 16, q=OUT, k=Kt, v=Vt)
+        a.update(kw)
+        return lib.st_qkv_rope_fwd(a["x"], a["w"], a["b"], a["T"], a["H"], a["W"], a["n_text"], a["heads"],
+                                   a["d"], sp(*a["split"]), a["theta"], a["dtype"], a["ws"], a["ws_bytes"],
+                                   a["q"], a["k"], a["v"], None)
+    assert f(x=None) == ST_ERR_NULL
+    assert f(v=None) == ST_ERR_NULL
+    assert f(T=0) == ST_ERR_SHAPE
+    assert f(split=(44, 42, 40)) == ST_ERR_SPLIT
+    assert f(d=64, split=(20, 22, 22)) == ST_ERR_UNSUPPORTED
+    assert f(theta=-1.0) == ST_ERR_UNSUPPORTED
+    assert f(ws_bytes=64) == ST_ERR_WORKSPACE
+    assert f(k=OUT + 512) == ST_ERR_ALIAS          # k overlaps q
+    assert f(q=Q + 1024) == ST_ERR_ALIAS           # q overlaps x
+    assert f(b=B + 4) == ST_ERR_ALIGN
+    assert f(w=Wt + 8) == ST_ERR_ALIGN
+    assert f(heads=100, T=64, H=64, W=64) == ST_ERR_SHAPE   # 32-bit offsets of the bf16 kernel
+    assert lib.st_qkv_rope_workspace_bytes(3, 4, 6, sp(44, 42, 42)) == lib.st_rope3d_table_bytes(3, 4, 6, sp(44, 42, 42))

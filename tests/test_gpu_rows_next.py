@@ -138,3 +138,73 @@ def test_merge_in_place_and_single_part(dtype):
     assert torch.equal(o_in, o_ref) and torch.equal(l_in, l_ref)
     assert float((o_one.float() - o0.float()).abs().max()) <= (2 ** -8 if dtype == "bf16" else 1e-6)
     assert float((l_one - l0).abs().max()) <= 1e-6
+
+
+# ---- QKV projection with the rotation of q and k ---------------------------------------------------
+
+def qkv_inputs(n, heads, dtype, seed, with_bias=True):
+    """x ~ N(0,1) [n, C], w ~ N(0, 1/C) [3C, C], bias ~ N(0, 0.1^2); bf16 inputs rounded once."""
+    from st_inputs import f32_to_bf16_bits, bf16_bits_to_f32
+    c = heads * 128
+    rng = np.random.default_rng(seed)
+    arrs = [rng.standard_normal((n, c)).astype(np.float32),
+            (rng.standard_normal((3 * c, c)) / np.sqrt(c)).astype(np.float32),
+            (0.1 * rng.standard_normal(3 * c)).astype(np.float32)]
+    if dtype == "bf16":
+        bits = [f32_to_bf16_bits(a) for a in arrs]
+        host = [bf16_bits_to_f32(b) for b in bits]
+        dev = [torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).cuda() for b in bits]
+    else:
+        host = arrs
+        dev = [torch.from_numpy(a).cuda() for a in arrs]
+    if not with_bias:
+        host[2], dev[2] = None, None
+    return host, dev
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("grid,n_text,heads,split,bias", [
+    ((3, 5, 7), 9, 2, WAN, True),
+    ((2, 16, 20), 0, 3, HUN, True),      # 3C = 1152: a partial feature tile
+    ((1, 1, 1), 0, 1, WAN, False),
+])
+def test_qkv_rope_small(dtype, grid, n_text, heads, split, bias):
+    n = grid[0] * grid[1] * grid[2] + n_text
+    log(f"  qkv_rope grid={grid} n_text={n_text} heads={heads} split={split} bias={bias} dtype={dtype} seed=7600")
+    (xh, wh, bh), (x, w, b) = qkv_inputs(n, heads, dtype, 7600, bias)
+    q, k, v = fa.qkv_rope(x, w, grid, bias=b, n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.qkv_rope_ref(xh, wh, bh, grid, n_text, split)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        assert_close(host_f64(got), ref, dtype, f"qkv_rope {name} {dtype}")
+
+
+def test_qkv_rope_wan13b_sampled():
+    """Wan2.1-1.3B-shaped projection: 32,760 tokens x 1,536 features -> 4,608, sampled rows."""
+    grid, heads = (21, 30, 52), 12
+    n = grid[0] * grid[1] * grid[2]
+    log(f"  qkv_rope grid={grid} heads={heads} dtype=bf16 seed=7700 rows=512")
+    (xh, wh, bh), (x, w, b) = qkv_inputs(n, heads, "bf16", 7700)
+    q, k, v = fa.qkv_rope(x, w, grid, bias=b, rope_split=WAN)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, n, 1560, 512, 7703)
+    rq, rk, rv = oracle.qkv_rope_ref(xh, wh, bh, grid, 0, WAN, rows=rows)
+    for name, got, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        assert_close(host_f64(got)[rows], ref, "bf16", f"qkv_rope 32760x1536 {name} sampled")
+
+
+def test_qkv_rope_then_attention_equals_full_3d_attention():
+    """Rotated q, k from the projection, then attention without rotation, against the oracle's
+    3D-RoPE attention of the projected (unrotated) x w^T."""
+    grid, n_text, heads, split = (3, 6, 8), 5, 2, WAN
+    n = grid[0] * grid[1] * grid[2] + n_text
+    log(f"  qkv_rope + attention grid={grid} n_text={n_text} heads={heads} seed=7800")
+    (xh, wh, _), (x, w, _) = qkv_inputs(n, heads, "bf16", 7800, with_bias=False)
+    q, k, v = fa.qkv_rope(x, w, grid, n_text=n_text, rope_split=split)
+    out = fa.attn_cross(q, k, v)
+    torch.cuda.synchronize()
+    c = heads * 128
+    y = np.asarray(xh, np.float64) @ np.asarray(wh, np.float64).T
+    ref = oracle.full_attention_ref(y[:, :c].reshape(n, heads, 128), y[:, c:2 * c].reshape(n, heads, 128),
+                                    y[:, 2 * c:].reshape(n, heads, 128), grid, n_text, split)
+    assert_close(host_f64(out), ref, "bf16", "qkv_rope then attention")
