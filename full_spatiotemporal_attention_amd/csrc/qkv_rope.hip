@@ -54,9 +54,18 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[G_LDS];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
+    // Tile order: each XCD takes a contiguous run of logical ids (xcd_remap), and consecutive ids
+    // walk GROUP token tiles for one feature tile before the next feature tile, so the 32 tiles
+    // an XCD runs at once share 8 x panels and 4 W panels through its L2.
     const int logical = xcd_remap(blockIdx.x, p.total_wg);
-    const int mt = logical / p.n_tiles;
-    const int nt = logical - mt * p.n_tiles;
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * p.n_tiles;
+    const int grp = logical / per_group;
+    const int first_m = grp * GROUP;
+    const int gsize = min(p.m_tiles - first_m, GROUP);
+    const int in_grp = logical - grp * per_group;
+    const int mt = first_m + in_grp % gsize;
+    const int nt = in_grp / gsize;
     const int m0 = mt * GM;                  // first token
     const int f0 = nt * GN;                  // first output feature
     const int C = p.C;
@@ -122,20 +131,34 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
     auto step = [&](auto stc, int ks) {
         constexpr int st = decltype(stc)::value;
         if (ks + 1 < ksteps) issue_stage(ks + 1, st ^ 1);
+        // Operands of k16 step kk+1 are read while the MFMAs of step kk run.
+        bf16x8_t a[2][2], b[2][4];
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) a[0][fb] = rd(a_rd[fb], st, 0);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) b[0][tb] = rd(b_rd[tb], st, 0);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            bf16x8_t a[2], b[4];
+            const int cur = kk & 1;
+            if (kk + 1 < 4) {
 #pragma unroll
-            for (int fb = 0; fb < 2; ++fb) a[fb] = rd(a_rd[fb], st, kk);
+                for (int fb = 0; fb < 2; ++fb) a[cur ^ 1][fb] = rd(a_rd[fb], st, kk + 1);
 #pragma unroll
-            for (int tb = 0; tb < 4; ++tb) b[tb] = rd(b_rd[tb], st, kk);
+                for (int tb = 0; tb < 4; ++tb) b[cur ^ 1][tb] = rd(b_rd[tb], st, kk + 1);
+            }
 #pragma unroll
             for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fb], b[tb], acc[fb][tb], 0, 0, 0);
-            // Keep the operand reads of one k16 step next to its MFMAs (register use).
-            asm volatile("" ::: "memory");
+                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][fb], b[cur][tb], acc[fb][tb], 0, 0, 0);
+            if (kk + 1 < 4) {
+#pragma unroll
+                for (int t = 0; t < 6; ++t) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
