@@ -76,12 +76,14 @@ def _normal(seed: int, shape) -> np.ndarray:
 
 def make_qkv(n_tokens: int, heads: int, d: int, seed_base: int, dtype: str = "bf16",
              row_scale: tuple[float, float] | None = None, v_offset: float = 0.0,
-             q_mult: float = 1.0) -> QKV:
+             q_mult: float = 1.0, k_ramp: float = 0.0) -> QKV:
     """Draw q, k, v ~ N(0, 1) of shape [n_tokens, heads, d].
 
     ``row_scale=(lo, hi)`` multiplies every (token, head) row of each tensor by an independent
     U(lo, hi) factor before rounding.  ``v_offset`` adds a constant to every v entry and ``q_mult``
     multiplies q, both before rounding (stress variants for normalisation and peaky softmax).
+    ``k_ramp`` multiplies k row n by 1 + k_ramp * n / n_tokens, so that scores grow along the
+    sequence and a running maximum keeps moving.
     """
     if dtype not in ("bf16", "f32"):
         raise ValueError(f"dtype must be 'bf16' or 'f32', got {dtype!r}")
@@ -100,6 +102,9 @@ def make_qkv(n_tokens: int, heads: int, d: int, seed_base: int, dtype: str = "bf
             x *= np.float32(q_mult)
         if i == 2 and v_offset != 0.0:
             x += np.float32(v_offset)
+        if i == 1 and k_ramp != 0.0:
+            ramp = 1.0 + k_ramp * np.arange(n_tokens, dtype=np.float64) / n_tokens
+            x *= ramp.astype(np.float32)[:, None, None]
         tensors.append(x)
     if dtype == "f32":
         return QKV(q=tensors[0], k=tensors[1], v=tensors[2], dtype="f32")

@@ -148,6 +148,25 @@ def test_stress_value_offset_and_peaky_queries():
     assert_close(got, ref, "bf16", "q*8")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_running_max_keeps_growing(dtype):
+    # Peaky queries against keys whose norm grows along the sequence: every few tiles a row's
+    # maximum moves past the stored one, so the rescale of the accumulator is taken many times.
+    # Scores reach |s| ~ 100 in log2 units here, far outside the N(0,1) workloads the 2e-2 bound
+    # is set for: fp16 rounding (2^-11) of rotated q and k moves such scores by up to ~0.05, which
+    # moves near-tied weights by up to ~3 %, times value differences of up to ~6.  bf16 is held
+    # to the relative-L2 bar and max-abs 5e-2.  In f32 the same scores carry ~100 x 2^-24 of
+    # rounding in the exponent, so f32 keeps relative L2 <= 1e-5 and max-abs <= 1e-4.
+    got, ref = run_full((4, 9, 10), 2, dtype, 305, q_mult=6.0, k_ramp=3.0)
+    assert np.isfinite(got).all()
+    max_abs, rel = errors(got, ref)
+    log(f"    growing maximum {dtype}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    if dtype == "f32":
+        assert rel <= 1e-5 and max_abs <= 1e-4
+    else:
+        assert rel <= 5e-3 and max_abs <= 5e-2
+
+
 def test_stage_attend_matches_fwd_bitwise():
     grid, heads = (5, 9, 11), 2
     x = make_qkv(495, heads, 128, 400, "bf16")
