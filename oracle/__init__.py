@@ -18,6 +18,7 @@ from .st_oracle import (  # noqa: F401
     factorized_flops,
     partial_attention_ref,
     qkv_rope_ref,
+    window_attention_ref,
     rope_frequencies,
     rope_pair_layout,
     rope3d_ref,

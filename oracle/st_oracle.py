@@ -31,6 +31,11 @@ What it computes, and where each step comes from (page title, then section):
   3.1 (the Wan block's projections Q = X W_Q, K = X W_K, V = X W_V) and the first page's cost
   model (the linear layers, 24 N D^2 per layer, of which the QKV projection is 6 N D^2); the
   rotation is the same 3D RoPE of q and k, applied to the projection's output.
+* Local 3D-window attention -- the CogVideoX record page (the W.A.L.T comparison alternates
+  per-frame spatial blocks with local 3D-window blocks): the grid is cut into non-overlapping
+  windows of wt x wh x ww tokens and every token attends to the tokens of its own window, with
+  the same rotated q and k.  Full attention is the one-window case and the factorised spatial
+  stage the (1, H', W') case.
 * Partial attention and its merge -- the CogVideoX record page ("Budget for that cost, because it
   grows": attention is split across devices by context parallelism, 2D ring and Ulysses) and the
   first page's shard listing under "Position: RoPE in three dimensions" (each device holds a
@@ -81,6 +86,7 @@ __all__ = [
     "partial_attention_ref",
     "merge_partials_ref",
     "qkv_rope_ref",
+    "window_attention_ref",
 ]
 
 
@@ -409,3 +415,32 @@ def qkv_rope_ref(x, w, bias, grid, n_text: int = 0, split=(44, 42, 42), theta: f
     v = y[:, 2 * c:].reshape(rows.size, heads, d)
     return (rope3d_ref(q, grid, n_text, split, theta, rows=rows),
             rope3d_ref(k, grid, n_text, split, theta, rows=rows), v)
+
+
+def window_attention_ref(q, k, v, grid, window, split=(44, 42, 42), theta: float = 10000.0, rows=None):
+    """Attention inside non-overlapping wt x wh x ww windows of the T' x H' x W' grid (no text).
+
+    Every row is rotated by its own (t, h, w); query row n attends to the rows whose
+    (t // wt, h // wh, w // ww) equal its own.  Returns [len(rows), heads, d] in float64.
+    """
+    t_, h_, w_ = grid
+    wt, wh, ww = window
+    if t_ % wt or h_ % wh or w_ % ww:
+        raise ValueError("window sizes must divide the grid")
+    n = t_ * h_ * w_
+    if q.shape[0] != n:
+        raise ValueError("q must have T'H'W' rows (no text rows)")
+    if rows is None:
+        rows = np.arange(n)
+    rows = np.asarray(rows)
+    t, h, w, _ = token_positions(grid)
+    win = (t // wt) * ((h_ // wh) * (w_ // ww)) + (h // wh) * (w_ // ww) + (w // ww)
+    qr = rope3d_ref(np.asarray(q, ORACLE_DTYPE), grid, 0, split, theta)
+    kr = rope3d_ref(np.asarray(k, ORACLE_DTYPE), grid, 0, split, theta)
+    vv = np.asarray(v, ORACLE_DTYPE)
+    out = np.empty((rows.size, q.shape[1], v.shape[-1]), dtype=ORACLE_DTYPE)
+    for wi in np.unique(win[rows]):
+        members = np.nonzero(win == wi)[0]
+        sel = np.nonzero(win[rows] == wi)[0]
+        out[sel] = attention_dense(qr[rows[sel]], kr[members], vv[members])
+    return out

@@ -714,3 +714,45 @@ def test_planted_qkv_mistakes_are_caught(mode):
     else:
         y = x @ w[c:2 * c].T
         assert np.abs(y.reshape(4, heads, d) - q).max() > 1e-3
+
+
+# ---- local 3D-window attention ---------------------------------------------------------------------
+
+def test_window_attention_equals_masked_sdpa():
+    """Against torch SDPA with an explicit same-window boolean mask (an independent routine)."""
+    rng = np.random.default_rng(91)
+    grid, window, split, heads, d = (4, 4, 6), (2, 2, 3), (4, 2, 2), 2, 8
+    n = 96
+    q, k, v = (rng.standard_normal((n, heads, d)) for _ in range(3))
+    got = oracle.window_attention_ref(q, k, v, grid, window, split)
+    t, h, w, _ = oracle.token_positions(grid)
+    key = np.stack([t // 2, h // 2, w // 3], 1)
+    mask = (key[:, None, :] == key[None, :, :]).all(-1)
+    qr = oracle.rope3d_ref(q, grid, 0, split)
+    kr = oracle.rope3d_ref(k, grid, 0, split)
+    qt = torch.from_numpy(np.ascontiguousarray(np.transpose(qr, (1, 0, 2))))
+    kt = torch.from_numpy(np.ascontiguousarray(np.transpose(kr, (1, 0, 2))))
+    vt = torch.from_numpy(np.ascontiguousarray(np.transpose(v, (1, 0, 2))))
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(mask))
+    np.testing.assert_allclose(got, np.transpose(ref.numpy(), (1, 0, 2)), rtol=1e-12, atol=1e-12)
+    rows = np.array([0, 17, 95])
+    np.testing.assert_allclose(oracle.window_attention_ref(q, k, v, grid, window, split, rows=rows), got[rows], atol=0)
+
+
+def test_window_attention_special_cases():
+    rng = np.random.default_rng(92)
+    grid, split, heads, d = (3, 4, 4), (4, 2, 2), 2, 8
+    n = 48
+    q, k, v = (rng.standard_normal((n, heads, d)) for _ in range(3))
+    # one window over the whole grid is full attention
+    np.testing.assert_allclose(oracle.window_attention_ref(q, k, v, grid, grid, split),
+                               oracle.full_attention_ref(q, k, v, grid, 0, split), rtol=1e-12, atol=1e-12)
+    # (1, H', W') windows are the factorised spatial stage
+    _, o_s = oracle.factorized_ref(q, k, v, grid, split, return_spatial=True)
+    spatial = np.stack([o_s[i] for i in range(n)])
+    np.testing.assert_allclose(oracle.window_attention_ref(q, k, v, grid, (1, 4, 4), split), spatial,
+                               rtol=1e-12, atol=1e-12)
+    # 1 x 1 x 1 windows: every token sees only itself
+    np.testing.assert_allclose(oracle.window_attention_ref(q, k, v, grid, (1, 1, 1), split), v, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.window_attention_ref(q, k, v, grid, (2, 4, 4), split)
