@@ -212,7 +212,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel<false>",
+            "kernel": "attn_fwd_kernel<false, false>",
             "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -321,6 +321,21 @@ def main():
         extras["qkv_rope_ms"] = round(qkv_ms, 4)
         extras["qkv_rope_TFLOPs"] = round(2.0 * n * C * 3 * C / (qkv_ms * 1e-3) / 1e12, 2)
         del xq, wq, bq
+        # Local 3D windows of 7 x 10 x 13 = 910 tokens (36 windows over the grid).
+        WIN = (7, 10, 13)
+        L_win = WIN[0] * WIN[1] * WIN[2]
+        wws = torch.empty(max(256, fa._lib.load().st_attn3d_window_workspace_bytes(
+            *GRID, HEADS, D, _lib.split_arg(SPLIT), _lib.split_arg(WIN), _lib.ST_BF16)), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            fa.attn_window(q, k, v, GRID, WIN, SPLIT, THETA, out=fout, workspace=wws)
+        e0.record(stream)
+        for _ in range(reps):
+            fa.attn_window(q, k, v, GRID, WIN, SPLIT, THETA, out=fout, workspace=wws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        win_ms = e0.elapsed_time(e1) / reps
+        extras["window_7x10x13_ms"] = round(win_ms, 4)
+        extras["window_7x10x13_TFLOPs"] = round(4.0 * n * L_win * HEADS * D / (win_ms * 1e-3) / 1e12, 2)
         result["extras"] = extras
         eprint(f"extras: {extras}")
 

@@ -19,6 +19,7 @@ __all__ = [
     "attn3d_stage",
     "attn3d_attend",
     "attn_factorized",
+    "attn_window",
     "attn_cross",
     "attn3d_partial",
     "attn_merge",
@@ -200,6 +201,29 @@ def attn_factorized(q, k, v, grid, rope_split=WAN_SPLIT, theta=10000.0, out=None
                                     ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
                                     _stream(q.device))
     _lib.check("st_attn_factorized_fwd", st)
+    return out
+
+
+def attn_window(q, k, v, grid, window, rope_split=WAN_SPLIT, theta=10000.0, out=None,
+                workspace=None) -> torch.Tensor:
+    """Attention inside non-overlapping (wt, wh, ww) windows of the grid, with 3D RoPE."""
+    lib = _lib.load()
+    T, H, W, heads, d = _check_tensors(grid, 0, q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensors(grid, 0, q, out)
+    win = _lib.split_arg(window)
+    nbytes = int(lib.st_attn3d_window_workspace_bytes(T, H, W, heads, d, _lib.split_arg(rope_split), win,
+                                                      _dtype_code(q)))
+    if nbytes == 0:
+        raise ValueError("invalid grid, window, split or dtype for window attention")
+    ws = _workspace(nbytes, q.device, workspace)
+    st = lib.st_attn3d_window_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, heads, d,
+                                  _lib.split_arg(rope_split), float(theta), win, _dtype_code(q),
+                                  ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
+                                  _stream(q.device))
+    _lib.check("st_attn3d_window_fwd", st)
     return out
 
 

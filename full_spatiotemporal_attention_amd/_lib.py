@@ -34,6 +34,8 @@ SIGNATURES = {
     "st_attn3d_fwd_fused": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p]),
     "st_attn_factorized_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _split, _i]),
     "st_attn_factorized_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p, _p]),
+    "st_attn3d_window_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _split, _split, _i]),
+    "st_attn3d_window_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _split, _f, _split, _i, _p, _sz, _p, _p]),
     "st_rope3d_apply": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _split, _f, _i, _p, _sz, _p]),
     "st_attn_cross_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "st_attn_cross_fwd": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p, _p]),

@@ -20,6 +20,11 @@
 // Q is rotated inside the attention kernel in both modes (once per workgroup); V is never
 // rotated and is read straight from the caller's tensor.
 //
+// Window mode (template flag WIN, staged K): the sequences are the local 3D windows of the grid
+// (the CogVideoX record page, "Conditions", local 3D-window blocks); each lane maps its window-
+// local row to a grid row for the Q load, the V tile copy and the output store, and the staging
+// kernel does the same for K.
+//
 // Design (one workgroup = 8 waves = 256 query rows of one head and one sequence):
 //  * Scores are formed transposed, S^T = K~ Q~^T: a lane owns one query column and 16 keys per
 //    32x32 block, so the softmax row max and row sum are in-lane plus one exchange between the
@@ -82,6 +87,7 @@ struct AttnParams {
     int k_tiles;
     int total_wg;
     float scale_log2;      // log2(e) / sqrt(D)
+    WinMap win;            // window mode only: segment s is window s, rows via win_origin/offset
 };
 
 struct PrepParams {
@@ -94,6 +100,7 @@ struct PrepParams {
     int n_segs;
     int kv_pos_base;
     int k_tiles;
+    WinMap win;            // window mode only
 };
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -141,8 +148,11 @@ constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
 
-template <bool FUSED>
+// WIN (staged K only): segment s is local window s of p.win, and query, value and output rows are
+// the window's grid rows (win_origin + win_offset) instead of a contiguous run of buffer rows.
+template <bool FUSED, bool WIN>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
+    static_assert(!(FUSED && WIN), "window mode reads staged K");
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
@@ -152,6 +162,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const int seg = rest % p.n_segs;
     const int head = rest / p.n_segs;
     const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
+    const int win0 = WIN ? win_origin(seg, p.win) : 0;   // window mode: grid row of local row 0
     const int seg_len = p.seg_len;
     const int q_len = p.q_len;
     const long long row_stride = (long long)p.heads * D;
@@ -187,13 +198,24 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     auto issue_tile = [&](int j, int slot) {
         const uint32_t kl = lds0 + slot * TILE_BYTES + (8 * wave) * 256;
         const uint32_t vl = lds0 + V_LDS_BASE + slot * TILE_BYTES + (8 * wave) * 256;
-        const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
         const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
+        if constexpr (WIN) {
+            // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = dr0 + 4 * i;
-            const int re = r < last ? r : last;
-            dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
+            for (int i = 0; i < 2; ++i) {
+                const int r = dr0 + 4 * i;
+                const int re = r < last ? r : last;
+                const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
+                dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+            }
+        } else {
+            const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = dr0 + 4 * i;
+                const int re = r < last ? r : last;
+                dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
+            }
         }
         if constexpr (!FUSED) {
             const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
@@ -236,7 +258,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 
     const int q_local = qt * BM + wave * 32 + l32;
     const bool q_valid = q_local < q_len;
-    const int q_row = seg * q_len + (q_valid ? q_local : 0);   // query buffer row
+    const int q_row = WIN ? win0 + win_offset(q_valid ? q_local : 0, p.win)
+                          : seg * q_len + (q_valid ? q_local : 0);   // query buffer row
     const int q_pos = p.q_pos_base + q_row;                    // its global row
     f16x8_t qreg[8];
     {
@@ -466,7 +489,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 }
 
 // Staging for the default mode: one workgroup per (head, segment, key tile) rotates the tile's
-// 64 K rows into fp16.  Rows past the segment are written as zeros.
+// 64 K rows into fp16.  Rows past the segment are written as zeros.  WIN: segment s is window s.
+template <bool WIN>
 __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
     const int tile = blockIdx.x;
     const int kt = tile % p.k_tiles;
@@ -482,7 +506,8 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
         const int r = id >> 4, c = id & 15;
         const int kl = kt * BN + r;
         const bool valid = kl < p.seg_len;
-        const int nb = seg * p.seg_len + (valid ? kl : 0);   // key buffer row
+        const int nb = WIN ? win_origin(seg, p.win) + win_offset(valid ? kl : 0, p.win)
+                           : seg * p.seg_len + (valid ? kl : 0);   // key buffer row
         const int n = p.kv_pos_base + nb;                    // its global row
         uint4 raw = valid ? ld16(p.k + nb * row_stride + (long long)head * D + 8 * c) : make_uint4(0, 0, 0, 0);
         int t = 0, h = 0, w = 0;
@@ -513,12 +538,13 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     p.k_tiles = (L.kv_len + BN - 1) / BN;
     p.total_wg = p.q_tiles * L.n_segs * heads;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
+    p.win = WinMap{};
     return p;
 }
 
 template <bool FUSED>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL(attn_fwd_kernel<FUSED>, dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, false>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -541,8 +567,42 @@ hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, c
     p.n_segs = L.n_segs;
     p.kv_pos_base = L.kv_pos_base;
     p.k_tiles = (L.kv_len + BN - 1) / BN;
+    p.win = WinMap{};
     const int blocks = heads * L.n_segs * p.k_tiles;
-    hipLaunchKernelGGL(k_prep_kernel, dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(k_prep_kernel<false>, dim3(blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
+                             int heads, const WinMap& m, int n_windows, int L, hipStream_t stream) {
+    PrepParams p;
+    p.k = k;
+    p.kt = kt;
+    p.table = table;
+    p.g = g;
+    p.heads = heads;
+    p.seg_len = L;
+    p.n_segs = n_windows;
+    p.kv_pos_base = 0;
+    p.k_tiles = (L + BN - 1) / BN;
+    p.win = m;
+    const int blocks = heads * n_windows * p.k_tiles;
+    hipLaunchKernelGGL(k_prep_kernel<true>, dim3(blocks), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
+                                uint16_t* out, const float2* table, const RopeGeom& g, int heads,
+                                const WinMap& m, int n_windows, int L, hipStream_t stream) {
+    SeqLayout sl;
+    sl.n_segs = n_windows;
+    sl.q_len = L;
+    sl.kv_len = L;
+    sl.q_pos_base = 0;
+    sl.kv_pos_base = 0;
+    AttnParams p = make_params(q, kt, v, out, nullptr, table, g, heads, sl);
+    p.win = m;
+    hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -1,9 +1,10 @@
 // fp32 checking kernel: 3D RoPE plus softmax attention over sets of rows, all in float32.
 //
-// Serves the ST_F32 mode of both entry points: full attention (one set of all N rows), the
-// factorised spatial stage (T sets of the H*W rows of a frame) and the temporal stage (H*W sets
+// Serves the ST_F32 mode of every entry point: full attention (one set of all N rows), the
+// factorised spatial stage (T sets of the H*W rows of a frame), the temporal stage (H*W sets
 // of the T rows at one position, "A video model's architecture: spatiotemporal attention and the
-// 3D VAE", self-test answer 2).  It is a correctness mode, not a fast path: one thread per query
+// 3D VAE", self-test answer 2), text cross-attention, runs of rows for partial results, and local
+// 3D windows (one set per window).  It is a correctness mode, not a fast path: one thread per query
 // row, rotated Q in LDS, K and V tiles in LDS, fp32 FMA dot products, expf.
 #include "st_internal.h"
 
@@ -48,12 +49,15 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
     const long long rs = (long long)p.heads * d;
     const RopeGeom& g = p.g;
     const F32Layout& L = p.L;
-    const int q0 = seq * L.q_mul;
-    const int kv0 = seq * L.kv_mul;
+    const int q0 = L.win ? win_origin(seq, L.wm) : seq * L.q_mul;
+    const int kv0 = L.win ? q0 : seq * L.kv_mul;
+    // buffer row of the i-th query (key) of this set
+    auto q_row_of = [&](int i) { return L.win ? q0 + win_offset(i, L.wm) : q0 + i * L.q_stride; };
+    auto kv_row_of = [&](int i) { return L.win ? kv0 + win_offset(i, L.wm) : kv0 + i * L.kv_stride; };
 
     const int qi = blockIdx.x * QB + tid;
     const bool qv = qi < L.q_len;
-    const int qrow = q0 + (qv ? qi : 0) * L.q_stride;   // query buffer row
+    const int qrow = q_row_of(qv ? qi : 0);   // query buffer row
     {
         int t, h, w;
         bool text;
@@ -78,7 +82,7 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
         for (int idx = tid; idx < nk * half; idx += QB) {
             const int r = idx / half;
             const int pp = idx - r * half;
-            const int krow = kv0 + (k0 + r) * L.kv_stride;   // key buffer row
+            const int krow = kv_row_of(k0 + r);   // key buffer row
             int t, h, w;
             bool text;
             row_pos(L.kv_pos_base + krow, g, t, h, w, text);

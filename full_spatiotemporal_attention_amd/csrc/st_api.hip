@@ -29,6 +29,25 @@ RopeGeom make_geom(int T, int H, int W, const int split[3]) {
     return g;
 }
 
+WinMap make_winmap(int T, int H, int W, int wt, int wh, int ww) {
+    (void)T;
+    WinMap m;
+    m.nW = W / ww;
+    m.nHW = (H / wh) * m.nW;
+    m.inv_nW = 1.0f / (float)m.nW;
+    m.inv_nHW = 1.0f / (float)m.nHW;
+    m.wS = wh * ww;
+    m.ww = ww;
+    m.inv_wS = 1.0f / (float)m.wS;
+    m.inv_ww = 1.0f / (float)ww;
+    m.A = H * W - wh * ww;
+    m.B = W - ww;
+    m.oa = wt * H * W;
+    m.ob = wh * W;
+    m.oc = ww;
+    return m;
+}
+
 }  // namespace st
 
 namespace {
@@ -130,6 +149,8 @@ st::F32Layout f32_layout(int n_seqs, int q_len, int q_mul, int q_stride, int kv_
     L.kv_mul = kv_mul;
     L.kv_stride = kv_stride;
     L.kv_pos_base = kv_pos_base;
+    L.win = 0;
+    L.wm = st::WinMap{};
     return L;
 }
 
@@ -361,6 +382,68 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_f32((const float*)q, (const float*)k, o_s, (float*)out, nullptr, table, g,
                                 heads, d, f32_layout(S, T, 1, S, T, 1, S), stream);
+    }
+    return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+size_t st_attn3d_window_workspace_bytes(int T, int H, int W, int heads, int d,
+                                        const int rope_split[3], const int window[3],
+                                        st_dtype dtype) {
+    long long n = 0;
+    if (!rope_split || !window || heads < 1 || !grid_ok(T, H, W, 0, &n)) return 0;
+    if (check_split(rope_split, d) != ST_OK) return 0;
+    const int dims[3] = {T, H, W};
+    for (int a = 0; a < 3; ++a)
+        if (window[a] < 1 || dims[a] % window[a]) return 0;
+    if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) : 0;
+    if (dtype != ST_BF16 || d != 128) return 0;
+    const int L = window[0] * window[1] * window[2];
+    return stage_layout(T, H, W, heads, L, (int)(n / L), rope_split).total;
+}
+
+st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                               int heads, int d, const int rope_split[3], float theta,
+                               const int window[3], st_dtype dtype, void* workspace,
+                               size_t ws_bytes, void* out, hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, 0, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!window) return ST_ERR_NULL;
+    const int dims[3] = {T, H, W};
+    for (int a = 0; a < 3; ++a)
+        if (window[a] < 1 || dims[a] % window[a]) return ST_ERR_SHAPE;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    if (!workspace) return ST_ERR_NULL;
+    if (!aligned(workspace, kWsAlign)) return ST_ERR_ALIGN;
+    const int L = window[0] * window[1] * window[2];
+    const int n_win = (int)(n / L);
+    // bf16: value rows are addressed with 32-bit byte offsets from the tensor base.
+    if (dtype == ST_BF16 && (unsigned long long)n * heads * d * 2 >= (1ULL << 32)) return ST_ERR_UNSUPPORTED;
+    if (dtype == ST_F32 && n_win > 65535) return ST_ERR_SHAPE;
+    size_t need = st_attn3d_window_workspace_bytes(T, H, W, heads, d, rope_split, window, dtype);
+    if (need == 0) return ST_ERR_SHAPE;
+    if (ws_bytes < need) return ST_ERR_WORKSPACE;
+    if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * elem_size(dtype), q, k, v, out))
+        return ST_ERR_ALIAS;
+    st::RopeGeom g = st::make_geom(T, H, W, rope_split);
+    st::WinMap m = st::make_winmap(T, H, W, window[0], window[1], window[2]);
+    char* ws = (char*)workspace;
+    float2* table = (float2*)ws;
+    hipError_t e = st::launch_rope_table(g, (double)theta, table, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dtype == ST_BF16) {
+        StageLayout SL = stage_layout(T, H, W, heads, L, n_win, rope_split);
+        uint16_t* kt = (uint16_t*)(ws + SL.table_bytes);
+        e = st::launch_k_prep_win((const uint16_t*)k, kt, table, g, heads, m, n_win, L, stream);
+        if (e != hipSuccess) return hip_fail(e);
+        e = st::launch_attn_bf16_win((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out, table, g,
+                                     heads, m, n_win, L, stream);
+    } else {
+        st::F32Layout FL = f32_layout(n_win, L, 0, 1, L, 0, 1);
+        FL.win = 1;
+        FL.wm = m;
+        e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
+                                table, g, heads, d, FL, stream);
     }
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }

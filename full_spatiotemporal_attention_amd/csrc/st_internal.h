@@ -42,6 +42,46 @@ __device__ __forceinline__ void decode_pos(int n, const RopeGeom& g, int& t, int
     t = q; h = qh; w = rw;
 }
 
+// Quotient and remainder of 0 <= n < 2^24 by d >= 1 through the fp32 reciprocal inv = fl(1/d)
+// and one correction step (the same argument as decode_pos).
+__device__ __forceinline__ int div_small(int n, int d, float inv, int& r) {
+    int q = (int)((float)n * inv);
+    r = n - q * d;
+    if (r < 0) { q -= 1; r += d; } else if (r >= d) { q += 1; r -= d; }
+    return q;
+}
+
+// Local 3D windows: the T x H x W grid cut into non-overlapping wt x wh x ww boxes, numbered
+// window-major (t-box, then h-box, then w-box); inside a window, tokens are numbered t-major
+// like the grid.  Token li of window s is the flat grid row origin(s) + offset(li).
+struct WinMap {
+    int nW, nHW;        // windows along w; windows per slab of wt frames
+    float inv_nW, inv_nHW;
+    int wS, ww;         // tokens per window frame (wh * ww); window width
+    float inv_wS, inv_ww;
+    int A, B;           // H*W - wh*ww and W - ww
+    int oa, ob, oc;     // origin steps per window index along t, h, w: wt*H*W, wh*W, ww
+};
+
+// Host-side construction (defined in st_api.hip).
+WinMap make_winmap(int T, int H, int W, int wt, int wh, int ww);
+
+__device__ __forceinline__ int win_origin(int s, const WinMap& m) {
+    int rem, c;
+    const int a = div_small(s, m.nHW, m.inv_nHW, rem);
+    const int b = div_small(rem, m.nW, m.inv_nW, c);
+    return a * m.oa + b * m.ob + c * m.oc;
+}
+
+// offset(li) = lt*H*W + lh*W + lw for li = (lt*wh + lh)*ww + lw, written as li + lt*A + lh*B.
+__device__ __forceinline__ int win_offset(int li, const WinMap& m) {
+    int rem, lw;
+    const int lt = div_small(li, m.wS, m.inv_wS, rem);
+    const int lh = div_small(rem, m.ww, m.inv_ww, lw);
+    (void)lw;
+    return li + lt * m.A + lh * m.B;
+}
+
 // Table entry of head pair `p` (0 .. d/2-1) for a row at (t, h, w); text rows get the identity.
 __device__ __forceinline__ int pair_entry(int p, int t, int h, int w, bool text, const RopeGeom& g) {
     int a = (p >= g.first[1]) + (p >= g.first[2]);
@@ -122,6 +162,15 @@ struct SeqLayout {
     int kv_pos_base;
 };
 
+// Local window attention over the video rows of a T x H x W grid, bf16, d = 128: one problem per
+// window of L = wt*wh*ww tokens (windows as in WinMap).  `kt` holds attn_stage_elems(heads, L,
+// n_windows) elements.
+hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
+                             int heads, const WinMap& m, int n_windows, int L, hipStream_t stream);
+hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
+                                uint16_t* out, const float2* table, const RopeGeom& g, int heads,
+                                const WinMap& m, int n_windows, int L, hipStream_t stream);
+
 // Flash attention for bf16 storage, d = 128.
 // Staged mode: launch_k_prep rotates K into fp16 tiles `kt` (attn_stage_elems(...) uint16
 // elements), then launch_attn_bf16_staged reads them together with V.
@@ -149,10 +198,14 @@ hipError_t launch_attn_temporal_bf16(const uint16_t* q, const uint16_t* k, const
 // (i < q_len) and key/value buffer rows s * kv_mul + j * kv_stride (j < kv_len), for s < n_seqs;
 // positions are buffer rows plus the two position bases.  Output (and lse) rows are the query
 // buffer rows.
+// With `win` set, problem s is window s of `wm` instead: query and key/value rows are both
+// win_origin(s) + win_offset(i) for i < q_len (= kv_len); the mul/stride fields are unused.
 struct F32Layout {
     int n_seqs;
     int q_len, q_mul, q_stride, q_pos_base;
     int kv_len, kv_mul, kv_stride, kv_pos_base;
+    int win;
+    WinMap wm;
 };
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, float* out, float* lse,
                            const float2* table, const RopeGeom& g, int heads, int d,

@@ -152,6 +152,30 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v,
                                  void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Local 3D-window attention (the CogVideoX record page, "Conditions": the W.A.L.T comparison
+ * alternates per-frame spatial blocks with local 3D-window blocks).  The T x H x W grid is cut
+ * into non-overlapping boxes of window[0] x window[1] x window[2] (t, h, w) tokens; each token
+ * attends, non-causally with scale 1/sqrt(d), to the tokens of its own box, with q and k rotated
+ * by their own (t, h, w) as in st_attn3d_fwd.  A window equal to the grid is full attention; a
+ * window of (1, H, W) is the first stage of st_attn_factorized_fwd.
+ *   q, k, v, out  [N][heads][d] in the flat grid order, N = T*H*W (no text rows); out must not
+ *                 overlap q, k or v.
+ *   window        {wt, wh, ww}, each >= 1 and dividing T, H, W respectively (else ST_ERR_SHAPE).
+ * ST_BF16: d == 128, numerics as st_attn3d_fwd, N*heads*d*2 bytes below 2^32 (else
+ * ST_ERR_UNSUPPORTED).  ST_F32: even d <= 128, at most 65535 windows.  Workspace (caller-owned,
+ * 256-byte aligned, st_attn3d_window_workspace_bytes bytes, 0 for an invalid request): the angle
+ * table and, for bf16, the rotated fp16 key tiles of every window.  Three launches (table, key
+ * staging, attention) on `stream`.
+ * ------------------------------------------------------------------------------------------- */
+size_t st_attn3d_window_workspace_bytes(int T, int H, int W, int heads, int d,
+                                        const int rope_split[3], const int window[3],
+                                        st_dtype dtype);
+st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
+                               int heads, int d, const int rope_split[3], float theta,
+                               const int window[3], st_dtype dtype, void* workspace,
+                               size_t ws_bytes, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Stand-alone 3D RoPE: y = R_3D(t, h, w) x for every row (text rows copied unchanged).
  * x and y: [N][heads][d]; y == x (in place) is allowed, other overlaps are not.  ST_BF16 needs
  * d % 8 == 0, ST_F32 needs d even.  Workspace: st_rope3d_table_bytes bytes.

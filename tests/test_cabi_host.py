@@ -355,3 +355,48 @@ def test_qkv_rope_rejects_invalid_arguments(lib):
     assert f(w=Wt + 8) == ST_ERR_ALIGN
     assert f(heads=100, T=64, H=64, W=64) == ST_ERR_SHAPE   # 32-bit offsets of the bf16 kernel
     assert lib.st_qkv_rope_workspace_bytes(3, 4, 6, sp(44, 42, 42)) == lib.st_rope3d_table_bytes(3, 4, 6, sp(44, 42, 42))
+
+
+def win(*w):
+    return _lib.split_arg(w)
+
+
+def test_window_workspace_bytes(lib):
+    tb = lib.st_rope3d_table_bytes(21, 30, 52, sp(44, 42, 42))
+    # 36 windows of 7 x 10 x 13 = 910 tokens: 15 key tiles of 64 rows each per window and head
+    tiles = (12 * 36 * 15 * 64 * 128 * 2 + 255) // 256 * 256
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 13), 0) == \
+        tb + tiles
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 13), 1) == tb
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 12), 0) == 0
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(0, 10, 13), 0) == 0
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), None, 0) == 0
+    assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 64, sp(22, 20, 22), win(7, 10, 13), 0) == 0
+
+
+def test_window_rejects_invalid_arguments(lib):
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, T=4, H=6, W=8, heads=2, d=128, split=(44, 42, 42), theta=1e4,
+                 window=(2, 3, 4), dtype=0, ws=WS, ws_bytes=1 << 24, out=OUT)
+        a.update(kw)
+        return lib.st_attn3d_window_fwd(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["heads"],
+                                        a["d"], sp(*a["split"]), a["theta"],
+                                        None if a["window"] is None else win(*a["window"]),
+                                        a["dtype"], a["ws"], a["ws_bytes"], a["out"], None)
+    assert f(q=None) == ST_ERR_NULL
+    assert f(window=None) == ST_ERR_NULL
+    assert f(ws=None) == ST_ERR_NULL
+    assert f(window=(3, 3, 4)) == ST_ERR_SHAPE       # 3 does not divide T = 4
+    assert f(window=(2, 0, 4)) == ST_ERR_SHAPE
+    assert f(window=(2, 3, -4)) == ST_ERR_SHAPE
+    assert f(split=(44, 42, 40)) == ST_ERR_SPLIT
+    assert f(d=64, split=(22, 20, 22)) == ST_ERR_UNSUPPORTED   # bf16 needs d == 128
+    assert f(theta=0.0) == ST_ERR_UNSUPPORTED
+    assert f(ws_bytes=1024) == ST_ERR_WORKSPACE
+    assert f(ws=WS + 8) == ST_ERR_ALIGN
+    assert f(out=V) == ST_ERR_ALIAS
+    assert f(ws=K) == ST_ERR_ALIAS
+    # bf16 value rows are addressed with 32-bit byte offsets: 2^32 bytes of V is refused
+    assert f(T=64, H=64, W=64, heads=64, window=(4, 4, 4), ws_bytes=1 << 40) == ST_ERR_UNSUPPORTED
+    # fp32: at most 65535 windows (one grid row of workgroups per window)
+    assert f(T=64, H=64, W=32, dtype=1, d=64, split=(22, 20, 22), window=(1, 1, 1)) == ST_ERR_SHAPE

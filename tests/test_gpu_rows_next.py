@@ -208,3 +208,57 @@ def test_qkv_rope_then_attention_equals_full_3d_attention():
     ref = oracle.full_attention_ref(y[:, :c].reshape(n, heads, 128), y[:, c:2 * c].reshape(n, heads, 128),
                                     y[:, 2 * c:].reshape(n, heads, 128), grid, n_text, split)
     assert_close(host_f64(out), ref, "bf16", "qkv_rope then attention")
+
+
+# ---- local 3D-window attention ------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("grid,window,split,heads", [
+    ((4, 6, 8), (2, 3, 4), WAN, 2),        # 24 tokens per window: one partial key tile
+    ((6, 10, 12), (3, 5, 6), HUN, 2),      # 90: a full tile and a ragged one
+    ((4, 16, 16), (2, 8, 16), WAN, 1),     # 256: exactly one query block
+    ((2, 9, 35), (1, 9, 35), WAN, 2),      # 315: the per-frame (spatial) case, two query blocks
+    ((3, 8, 12), (3, 8, 12), HUN, 2),      # one window over the whole grid
+])
+def test_window_matches_oracle(dtype, grid, window, split, heads):
+    log(f"  window grid={grid} window={window} split={split} heads={heads} dtype={dtype} seed=7600")
+    x, (q, k, v) = grid_inputs(grid, 0, heads, dtype, 7600, split)
+    out = fa.attn_window(q, k, v, grid, window, rope_split=split)
+    torch.cuda.synchronize()
+    ref = oracle.window_attention_ref(x.q, x.k, x.v, grid, window, split)
+    assert_close(host_f64(out), ref, dtype, f"window {grid}/{window} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_of_one_token_returns_v(dtype):
+    """Each token alone in its window: its only weight is exp(0) = 1, so out == v exactly."""
+    grid = (3, 5, 7)
+    log(f"  window grid={grid} window=(1,1,1) dtype={dtype} seed=7610")
+    x, (q, k, v) = grid_inputs(grid, 0, 2, dtype, 7610, WAN)
+    out = fa.attn_window(q, k, v, grid, (1, 1, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(out, v)
+
+
+def test_window_over_whole_grid_is_full_attention_bitwise():
+    """With one window the row map is the identity and the kernel does the full path's arithmetic."""
+    grid = (3, 10, 13)
+    log(f"  window grid={grid} window=grid vs attn3d dtype=bf16 seed=7620")
+    _, (q, k, v) = grid_inputs(grid, 0, 3, "bf16", 7620, WAN)
+    a = fa.attn_window(q, k, v, grid, grid)
+    b = fa.attn3d(q, k, v, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_window_wan_grid_sampled():
+    """21x30x52 grid (Wan 2.1, 81 frames at 480x832), 12 heads, windows of 7x10x13 = 910 tokens."""
+    grid, window, heads = (21, 30, 52), (7, 10, 13), 12
+    n = 32760
+    log(f"  window grid={grid} window={window} heads={heads} dtype=bf16 seed=7630 rows=512")
+    x, (q, k, v) = grid_inputs(grid, 0, heads, "bf16", 7630, WAN)
+    out = fa.attn_window(q, k, v, grid, window)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, n, 1560, 512, 7633)
+    ref = oracle.window_attention_ref(x.q, x.k, x.v, grid, window, WAN, rows=rows)
+    assert_close(host_f64(out)[rows], ref, "bf16", "window 21x30x52 / 7x10x13 sampled")
