@@ -8,7 +8,8 @@
 // of one frame (the spatial stage of factorised attention, "How attention sees time").
 //
 // Numerics: rotated q and k are rounded once to fp16 (11 significant bits) for the score product
-// (v_mfma_f32_32x32x16_f16, same rate as bf16); softmax weights are rounded to bf16 and multiply
+// (v_mfma_f32_32x32x16_f16, same rate as bf16); q is multiplied by log2(e)/sqrt(128) before that
+// rounding, so scores come out in log2 units.  Softmax weights are rounded to bf16 and multiply
 // the exact bf16 values (v_mfma_f32_32x32x16_bf16); accumulation, the running max and the row
 // sums are fp32, and the row sum adds exactly the rounded weights the product used.
 //
@@ -40,9 +41,10 @@
 //  * The score product of tile j+1 is issued before the softmax of tile j, so the MFMA pipe has
 //    work while the VALU computes exponentials.  The loop is unrolled by the buffer count so all
 //    LDS addresses are a per-lane base plus an immediate.
-//  * Online softmax with a lazily updated running max: the accumulator is rescaled only when a
-//    row max exceeds the stored one by more than 2^8 (exact in any case; the stored max is only
-//    an offset for the exponentials).
+//  * Online softmax with a lazily updated running max m: the accumulator is rescaled only when a
+//    row max exceeds m by more than 8 (log2 units; exact in any case, m is only an offset for the
+//    exponentials).  The score MFMAs start from -m instead of zero, so they return s - m and the
+//    exponentials need no subtraction.
 #include <type_traits>
 
 #include "st_internal.h"
@@ -59,7 +61,7 @@ constexpr int NBUF = 4;                          // tile j lives in K and V slot
 constexpr int PREF = 3;                          // step j fetches tile j + PREF
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
-constexpr float LAZY_LOG2 = 8.0f;  // rescale when the max grows by more than this (log2 units)
+constexpr float LAZY_LOG2 = 8.0f;  // move the offset when a row max exceeds it by more than this
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
@@ -112,14 +114,15 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 // Rotate 8 bf16 channels (pairs 4c .. 4c+3) of a row at (t, h, w) and return them as fp16.
 __device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, int w, bool text,
-                                                const RopeGeom& g, const float2* __restrict__ table) {
+                                                const RopeGeom& g, const float2* __restrict__ table,
+                                                float scale = 1.0f) {
     uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         float2 cs = table[pair_entry(4 * c + i, t, h, w, text, g)];
         float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
         rotate_pair(x0, x1, cs);
-        wd[i] = pack_f16x2(x0, x1);
+        wd[i] = pack_f16x2(x0 * scale, x1 * scale);
     }
     return make_uint4(wd[0], wd[1], wd[2], wd[3]);
 }
@@ -271,7 +274,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         for (int ks = 0; ks < 8; ++ks) {
             const int c = 2 * ks + hh;
             uint4 raw = q_valid ? ld16(qp + 8 * c) : make_uint4(0, 0, 0, 0);
-            qreg[ks] = __builtin_bit_cast(f16x8_t, rope_chunk_f16(raw, c, t, h, w, text, g, p.table));
+            qreg[ks] = __builtin_bit_cast(f16x8_t, rope_chunk_f16(raw, c, t, h, w, text, g, p.table,
+                                                                  p.scale_log2));
         }
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -337,10 +341,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
-    float m_run = -INFINITY;
+    // Scores are in log2 units (q carries log2(e)/sqrt(D)).  m_run is the offset already taken
+    // off every score: the score MFMAs start from negm = -m_run instead of zero.
+    float m_run = 0.0f;
     float l_run = 0.0f;
-    const float sl2 = p.scale_log2;
-    const float lazy_raw = LAZY_LOG2 / sl2;
+    f32x16_t negm;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
     const bool ragged = (seg_len % BN) != 0;
     const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
@@ -366,30 +373,32 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         constexpr int b1 = (b + 1) % NBUF;
         constexpr int bp = (b + PREF) % NBUF;
         if (ragged && j == ntiles - 1) mask_tail(j, sc);
-        const float mx = row_max(sc);
-        // Lazy running max: rescale the accumulator only when this tile's max is well above it.
-        const bool grow = mx > m_run + lazy_raw;
+        const float mx = row_max(sc);   // relative to m_run
+        // Lazy running max: move the offset only when this tile's max is well above it (and on
+        // the first tile, whose scores carry no offset yet).
+        const bool grow = (j == 0) | (mx > LAZY_LOG2);
         if (__any(grow)) {
-            const float m_new = grow ? mx : m_run;
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-            m_run = m_new;
+            const float dm = grow ? mx : 0.0f;
+            const float alpha = j == 0 ? 1.0f : __builtin_amdgcn_exp2f(-dm);
+            m_run += dm;
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sc[mb][i] -= dm;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) negm[i] = -m_run;
         }
-        const float mneg = -m_run * sl2;
 
         // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
         // last tile the K slot holds stale data and these scores are discarded.
         f16x8_t ka[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sn[mb][i] = 0.0f;
         bf16x8_t pb[4];
         float lpart[4];
 #pragma unroll
@@ -399,8 +408,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             float ls = 0.0f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[mb][o + 2 * e], sl2, mneg));
-                const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[mb][o + 2 * e + 1], sl2, mneg));
+                const float p0 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e]);
+                const float p1 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e + 1]);
                 u[e] = pack_bf16x2(p0, p1);
                 ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
                                                      __builtin_bit_cast(bf16x2_t, one2), ls, false);
@@ -409,8 +418,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
         }
         l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
+        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
+        for (int t = 2; t < 16; ++t)
             sn[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sn[t & 1], 0, 0, 0);
         __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
@@ -472,7 +483,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const float l_tot = xhalf_sum(l_run);
     const float inv = 1.0f / l_tot;
     if (p.lse && q_valid && hh == 0)
-        p.lse[(long long)q_row * p.heads + head] = m_run * (sl2 * 0.6931471805599453f) + __logf(l_tot);
+        p.lse[(long long)q_row * p.heads + head] = m_run * 0.6931471805599453f + __logf(l_tot);
     if (q_valid) {
         uint16_t* op = p.out + q_row * row_stride + (long long)head * D;
 #pragma unroll
