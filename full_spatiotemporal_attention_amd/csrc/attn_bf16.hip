@@ -266,16 +266,39 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     const int q_pos = p.q_pos_base + q_row;                    // its global row
     f16x8_t qreg[8];
     {
-        int t = 0, h = 0, w = 0;
+        // Lanes past the sequence read its first row (in bounds) and are never stored.  Pair p of
+        // the row reads table entry base_a + p, a the axis p falls in: the three bases are formed
+        // once per row, and each pair costs two compares and two selects.  Text rows take
+        // position (0, 0, 0), where every angle is 0 (cos 1, sin 0 exactly): no rotation.
         const bool text = q_pos >= g.Nv;
-        if (!text) decode_pos(q_pos, g, t, h, w);
-        const uint16_t* qp = p.q + q_row * row_stride + (long long)head * D;
+        int t, h, w;
+        decode_pos(text ? 0 : q_pos, g, t, h, w);
+        const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
+        const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
+        const int lane_p = 4 * hh;   // this lane half's pairs are 8 ks + 4 hh + i
+        const int bt = (int)__umul24((unsigned)t, (unsigned)g.pairs[0]) + lane_p;
+        const int bh = g.off[1] - f1 + (int)__umul24((unsigned)h, (unsigned)g.pairs[1]) + lane_p;
+        const int bw = g.off[2] - f2 + (int)__umul24((unsigned)w, (unsigned)g.pairs[2]) + lane_p;
+        const int g1 = f1 - lane_p, g2 = f2 - lane_p;
+        const float sc = p.scale_log2;
+        const uint16_t* qp = p.q + q_row * row_stride + (long long)head * D + 8 * hh;
+        uint4 raw[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) raw[ks] = ld16(qp + 16 * ks);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const int c = 2 * ks + hh;
-            uint4 raw = q_valid ? ld16(qp + 8 * c) : make_uint4(0, 0, 0, 0);
-            qreg[ks] = __builtin_bit_cast(f16x8_t, rope_chunk_f16(raw, c, t, h, w, text, g, p.table,
-                                                                  p.scale_log2));
+            const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p0 = 8 * ks + i;
+                const int base = p0 >= g2 ? bw : (p0 >= g1 ? bh : bt);
+                const float2 cs = p.table[base + p0];
+                float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
+                rotate_pair(x0, x1, cs);
+                o[i] = pack_f16x2(x0 * sc, x1 * sc);
+            }
+            qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
         }
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -553,8 +576,13 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     return p;
 }
 
+// The Q rotation reads table entry base_axis + pair for every pair of the head: the split must
+// cover all D/2 pairs (text rows read the position-0 entries).
+bool geom_covers_head(const RopeGeom& g) { return g.pairs[0] + g.pairs[1] + g.pairs[2] == D / 2; }
+
 template <bool FUSED>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
+    if (!geom_covers_head(p.g)) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attn_fwd_kernel<FUSED, false>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
@@ -611,6 +639,7 @@ hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uin
     sl.kv_len = L;
     sl.q_pos_base = 0;
     sl.kv_pos_base = 0;
+    if (!geom_covers_head(g)) return hipErrorInvalidValue;
     AttnParams p = make_params(q, kt, v, out, nullptr, table, g, heads, sl);
     p.win = m;
     hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);

@@ -154,6 +154,13 @@ st::F32Layout f32_layout(int n_seqs, int q_len, int q_mul, int q_stride, int kv_
     return L;
 }
 
+// Table of the cross-attention geometry (1x1x1 grid, every pair on the t axis): d/2 zero angles
+// and the identity entry.
+size_t cross_table_bytes(int d) {
+    const int t_only[3] = {d, 0, 0};
+    return table_bytes_for(1, 1, 1, t_only);
+}
+
 st_status hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
     return ST_ERR_HIP;
@@ -488,7 +495,8 @@ st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_tex
 size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dtype dtype) {
     if (n_q < 1 || n_kv < 1 || n_q >= kMaxRows || n_kv >= kMaxRows || heads < 1 || heads > 65535)
         return 0;
-    const size_t table = align_up(sizeof(float2), kWsAlign);
+    if (d < 2 || (d & 1)) return 0;
+    const size_t table = cross_table_bytes(d);
     if (dtype == ST_F32) return (d >= 2 && !(d & 1) && d <= 128) ? table : 0;
     if (dtype != ST_BF16 || d != 128) return 0;
     return table + align_up(st::attn_stage_elems(heads, n_kv, 1) * 2, kWsAlign);
@@ -518,9 +526,11 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
     if (overlaps(workspace, ws_bytes, q, qb) || overlaps(workspace, ws_bytes, out, qb) ||
         overlaps(workspace, ws_bytes, k, kb) || overlaps(workspace, ws_bytes, v, kb))
         return ST_ERR_ALIAS;
-    // A geometry with no video rows: every row is left unrotated (the identity table entry).
-    const int none[3] = {0, 0, 0};
-    st::RopeGeom g = st::make_geom(1, 1, 1, none);
+    // A geometry with no video rows: every row is a text row, which the kernels treat as
+    // position (0, 0, 0) or the identity entry; the table of a 1x1x1 grid with all pairs on the
+    // t axis holds only zero angles.
+    const int t_only[3] = {d, 0, 0};
+    st::RopeGeom g = st::make_geom(1, 1, 1, t_only);
     g.Nv = 0;
     char* ws = (char*)workspace;
     float2* table = (float2*)ws;
@@ -533,7 +543,7 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
         L.kv_len = n_kv;
         L.q_pos_base = 0;
         L.kv_pos_base = 0;
-        uint16_t* kt = (uint16_t*)(ws + align_up(sizeof(float2), kWsAlign));
+        uint16_t* kt = (uint16_t*)(ws + cross_table_bytes(d));
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out,

@@ -251,8 +251,9 @@ LSE = 0x600000000
 def test_cross_workspace_bytes(lib):
     wb = lib.st_attn_cross_workspace_bytes(1000, 77, 3, 128, 0)
     tiles = 3 * ((77 + 63) // 64) * 64 * 128 * 2
-    assert wb == 256 + ((tiles + 255) // 256) * 256
-    assert lib.st_attn_cross_workspace_bytes(1000, 77, 3, 64, 1) == 256
+    # table: d/2 zero angles plus the identity entry, 8 bytes each, rounded up to 256 B
+    assert wb == 768 + ((tiles + 255) // 256) * 256
+    assert lib.st_attn_cross_workspace_bytes(1000, 77, 3, 64, 1) == 512
     assert lib.st_attn_cross_workspace_bytes(1000, 77, 3, 64, 0) == 0      # bf16 needs d == 128
     assert lib.st_attn_cross_workspace_bytes(0, 77, 3, 128, 0) == 0
     assert lib.st_attn_cross_workspace_bytes(10, 0, 3, 128, 0) == 0
