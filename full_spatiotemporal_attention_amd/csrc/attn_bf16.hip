@@ -26,7 +26,8 @@
 // local row to a grid row for the Q load, the V tile copy and the output store, and the staging
 // kernel does the same for K.
 //
-// Design (one workgroup = 8 waves = 256 query rows of one head and one sequence):
+// Design (one item = 256 query rows of one head and one sequence, taken by a workgroup of 8 waves;
+// the launch is persistent: one workgroup per CU loops over items):
 //  * Scores are formed transposed, S^T = K~ Q~^T: a lane owns one query column and 16 keys per
 //    32x32 block, so the softmax row max and row sum are in-lane plus one exchange between the
 //    two 32-lane halves (v_permlane32_swap).
@@ -159,367 +160,371 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
-    const int logical = xcd_remap(blockIdx.x, p.total_wg);
-    const int qt = logical % p.q_tiles;
-    const int rest = logical / p.q_tiles;
-    const int seg = rest % p.n_segs;
-    const int head = rest / p.n_segs;
-    const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
-    const int win0 = WIN ? win_origin(seg, p.win) : 0;   // window mode: grid row of local row 0
-    const int seg_len = p.seg_len;
-    const int q_len = p.q_len;
-    const long long row_stride = (long long)p.heads * D;
-    const int ntiles = p.k_tiles;
+    // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
+    // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
+    for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
+        const int logical = xcd_remap(item, p.total_wg);
+        const int qt = logical % p.q_tiles;
+        const int rest = logical / p.q_tiles;
+        const int seg = rest % p.n_segs;
+        const int head = rest / p.n_segs;
+        const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
+        const int win0 = WIN ? win_origin(seg, p.win) : 0;   // window mode: grid row of local row 0
+        const int seg_len = p.seg_len;
+        const int q_len = p.q_len;
+        const long long row_stride = (long long)p.heads * D;
+        const int ntiles = p.k_tiles;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l32 = lane & 31;
-    const int hh = lane >> 5;
-    const RopeGeom& g = p.g;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l32 = lane & 31;
+        const int hh = lane >> 5;
+        const RopeGeom& g = p.g;
 
-    // ---- tile copies ------------------------------------------------------------------------
-    // Wave w, copy i in {0,1}: rows r = 8w + 4i + lane/16, physical chunk lane%16 of that row.
-    const int dr0 = 8 * wave + (lane >> 4);
-    const int pc = lane & 15;
-    const uint16_t* vhead = p.v + (long long)head * D;
-    const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
-    uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
-    int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
+        // ---- tile copies ------------------------------------------------------------------------
+        // Wave w, copy i in {0,1}: rows r = 8w + 4i + lane/16, physical chunk lane%16 of that row.
+        const int dr0 = 8 * wave + (lane >> 4);
+        const int pc = lane & 15;
+        const uint16_t* vhead = p.v + (long long)head * D;
+        const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
+        uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
+        int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r = dr0 + 4 * i;
-        k_src_off[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ k_swz(r)));
-        v_chunk[i] = 8 * (pc ^ v_swz(r));
-    }
-    // FUSED K copy through registers: thread owns chunks c = tid & 15 of rows tid>>4 and +32.
-    const int fkc = tid & 15;
-    const int fkr = tid >> 4;
-    uint4 fk0 = make_uint4(0, 0, 0, 0), fk1 = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const int r = dr0 + 4 * i;
+            k_src_off[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ k_swz(r)));
+            v_chunk[i] = 8 * (pc ^ v_swz(r));
+        }
+        // FUSED K copy through registers: thread owns chunks c = tid & 15 of rows tid>>4 and +32.
+        const int fkc = tid & 15;
+        const int fkr = tid >> 4;
+        uint4 fk0 = make_uint4(0, 0, 0, 0), fk1 = make_uint4(0, 0, 0, 0);
 
-    // issue_tile(j, slot): fetch tile j into K and V slot `slot`.
-    auto issue_tile = [&](int j, int slot) {
-        const uint32_t kl = lds0 + slot * TILE_BYTES + (8 * wave) * 256;
-        const uint32_t vl = lds0 + V_LDS_BASE + slot * TILE_BYTES + (8 * wave) * 256;
-        const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
-        if constexpr (WIN) {
-            // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
+        // issue_tile(j, slot): fetch tile j into K and V slot `slot`.
+        auto issue_tile = [&](int j, int slot) {
+            const uint32_t kl = lds0 + slot * TILE_BYTES + (8 * wave) * 256;
+            const uint32_t vl = lds0 + V_LDS_BASE + slot * TILE_BYTES + (8 * wave) * 256;
+            const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
+            if constexpr (WIN) {
+                // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = dr0 + 4 * i;
-                const int re = r < last ? r : last;
-                const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
-                dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+                for (int i = 0; i < 2; ++i) {
+                    const int r = dr0 + 4 * i;
+                    const int re = r < last ? r : last;
+                    const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
+                    dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+                }
+            } else {
+                const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = dr0 + 4 * i;
+                    const int re = r < last ? r : last;
+                    dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
+                }
             }
-        } else {
-            const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
+            if constexpr (!FUSED) {
+                const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = dr0 + 4 * i;
-                const int re = r < last ? r : last;
-                dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
+                for (int i = 0; i < 2; ++i) dma16(kt, k_src_off[i], kl + i * 1024);
+            } else {
+                const uint16_t* kh = p.k + (long long)head * D;
+                const int k0 = j * BN + fkr, k1 = k0 + 32;
+                fk0 = k0 < seg_len ? ld16(kh + (seg_base + k0) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
+                fk1 = k1 < seg_len ? ld16(kh + (seg_base + k1) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
+            }
+        };
+        // FUSED only: rotate the K registers fetched by issue_tile(j, slot) and write them to LDS.
+        auto finish_tile = [&](int j, int slot) {
+            if constexpr (FUSED) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = fkr + 32 * i;
+                    const int n = p.kv_pos_base + seg_base + j * BN + r;
+                    int t = 0, h = 0, w = 0;
+                    const bool text = n >= g.Nv;
+                    if (!text) decode_pos(n, g, t, h, w);
+                    uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, text, g, p.table);
+                    const uint32_t a = lds0 + slot * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
+                    const u32x4_t rv = {rot.x, rot.y, rot.z, rot.w};
+                    *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)a = rv;
+                }
+            } else {
+                (void)j;
+                (void)slot;
+            }
+        };
+
+        // ---- prologue -----------------------------------------------------------------------------
+#pragma unroll
+        for (int j = 0; j < PREF; ++j) {
+            issue_tile(min(j, ntiles - 1), j);
+            finish_tile(min(j, ntiles - 1), j);
+        }
+
+        const int q_local = qt * BM + wave * 32 + l32;
+        const bool q_valid = q_local < q_len;
+        const int q_row = WIN ? win0 + win_offset(q_valid ? q_local : 0, p.win)
+                              : seg * q_len + (q_valid ? q_local : 0);   // query buffer row
+        const int q_pos = p.q_pos_base + q_row;                    // its global row
+        f16x8_t qreg[8];
+        {
+            // Lanes past the sequence read its first row (in bounds) and are never stored.  Pair p of
+            // the row reads table entry base_a + p, a the axis p falls in: the three bases are formed
+            // once per row, and each pair costs two compares and two selects.  Text rows take
+            // position (0, 0, 0), where every angle is 0 (cos 1, sin 0 exactly): no rotation.
+            const bool text = q_pos >= g.Nv;
+            int t, h, w;
+            decode_pos(text ? 0 : q_pos, g, t, h, w);
+            const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
+            const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
+            const int lane_p = 4 * hh;   // this lane half's pairs are 8 ks + 4 hh + i
+            const int bt = (int)__umul24((unsigned)t, (unsigned)g.pairs[0]) + lane_p;
+            const int bh = g.off[1] - f1 + (int)__umul24((unsigned)h, (unsigned)g.pairs[1]) + lane_p;
+            const int bw = g.off[2] - f2 + (int)__umul24((unsigned)w, (unsigned)g.pairs[2]) + lane_p;
+            const int g1 = f1 - lane_p, g2 = f2 - lane_p;
+            const float sc = p.scale_log2;
+            const uint16_t* qp = p.q + q_row * row_stride + (long long)head * D + 8 * hh;
+            uint4 raw[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) raw[ks] = ld16(qp + 16 * ks);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+                uint32_t o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int p0 = 8 * ks + i;
+                    const int base = p0 >= g2 ? bw : (p0 >= g1 ? bh : bt);
+                    const float2 cs = p.table[base + p0];
+                    float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
+                    rotate_pair(x0, x1, cs);
+                    o[i] = pack_f16x2(x0 * sc, x1 * sc);
+                }
+                qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
             }
         }
-        if constexpr (!FUSED) {
-            const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) dma16(kt, k_src_off[i], kl + i * 1024);
-        } else {
-            const uint16_t* kh = p.k + (long long)head * D;
-            const int k0 = j * BN + fkr, k1 = k0 + 32;
-            fk0 = k0 < seg_len ? ld16(kh + (seg_base + k0) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
-            fk1 = k1 < seg_len ? ld16(kh + (seg_base + k1) * row_stride + 8 * fkc) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    // FUSED only: rotate the K registers fetched by issue_tile(j, slot) and write them to LDS.
-    auto finish_tile = [&](int j, int slot) {
-        if constexpr (FUSED) {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = fkr + 32 * i;
-                const int n = p.kv_pos_base + seg_base + j * BN + r;
-                int t = 0, h = 0, w = 0;
-                const bool text = n >= g.Nv;
-                if (!text) decode_pos(n, g, t, h, w);
-                uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, text, g, p.table);
-                const uint32_t a = lds0 + slot * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
-                const u32x4_t rv = {rot.x, rot.y, rot.z, rot.w};
-                *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)a = rv;
-            }
-        } else {
-            (void)j;
-            (void)slot;
-        }
-    };
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
 
-    // ---- prologue -----------------------------------------------------------------------------
+        // ---- per-lane LDS read addresses (slot 0; other slots add a multiple of TILE_BYTES) --------
+        // K operand of the score product: row l32 (+32 for the second block), logical chunk 2ks + hh.
+        uint32_t k_rd[8];
 #pragma unroll
-    for (int j = 0; j < PREF; ++j) {
-        issue_tile(min(j, ntiles - 1), j);
-        finish_tile(min(j, ntiles - 1), j);
-    }
-
-    const int q_local = qt * BM + wave * 32 + l32;
-    const bool q_valid = q_local < q_len;
-    const int q_row = WIN ? win0 + win_offset(q_valid ? q_local : 0, p.win)
-                          : seg * q_len + (q_valid ? q_local : 0);   // query buffer row
-    const int q_pos = p.q_pos_base + q_row;                    // its global row
-    f16x8_t qreg[8];
-    {
-        // Lanes past the sequence read its first row (in bounds) and are never stored.  Pair p of
-        // the row reads table entry base_a + p, a the axis p falls in: the three bases are formed
-        // once per row, and each pair costs two compares and two selects.  Text rows take
-        // position (0, 0, 0), where every angle is 0 (cos 1, sin 0 exactly): no rotation.
-        const bool text = q_pos >= g.Nv;
-        int t, h, w;
-        decode_pos(text ? 0 : q_pos, g, t, h, w);
-        const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
-        const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
-        const int lane_p = 4 * hh;   // this lane half's pairs are 8 ks + 4 hh + i
-        const int bt = (int)__umul24((unsigned)t, (unsigned)g.pairs[0]) + lane_p;
-        const int bh = g.off[1] - f1 + (int)__umul24((unsigned)h, (unsigned)g.pairs[1]) + lane_p;
-        const int bw = g.off[2] - f2 + (int)__umul24((unsigned)w, (unsigned)g.pairs[2]) + lane_p;
-        const int g1 = f1 - lane_p, g2 = f2 - lane_p;
-        const float sc = p.scale_log2;
-        const uint16_t* qp = p.q + q_row * row_stride + (long long)head * D + 8 * hh;
-        uint4 raw[8];
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) raw[ks] = ld16(qp + 16 * ks);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
-            uint32_t o[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p0 = 8 * ks + i;
-                const int base = p0 >= g2 ? bw : (p0 >= g1 ? bh : bt);
-                const float2 cs = p.table[base + p0];
-                float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
-                rotate_pair(x0, x1, cs);
-                o[i] = pack_f16x2(x0 * sc, x1 * sc);
-            }
-            qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-
-    // ---- per-lane LDS read addresses (slot 0; other slots add a multiple of TILE_BYTES) --------
-    // K operand of the score product: row l32 (+32 for the second block), logical chunk 2ks + hh.
-    uint32_t k_rd[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) k_rd[ks] = lds0 + l32 * 256 + 16 * ((2 * ks + hh) ^ k_swz(l32));
-    // V operand of the PV product, read transposed: lane (i = lane%16, g = lane/16) points at row
-    // 4*(g/2) + i/4 (+ 16 per key chunk, + 8 for the upper half) and channels 32 db + 16*(g%2) +
-    // 4*(i%4), i.e. logical chunk 4 db + 2*(g%2) + (i%4)/2, byte 8*(i%2) inside it.
-    uint32_t v_rd[4];
-    {
-        const int i = lane & 15, gq = lane >> 4;
-        const int row = 4 * (gq >> 1) + (i >> 2);
-        const int u = 2 * (gq & 1) + ((i & 3) >> 1);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-            v_rd[db] = lds0 + V_LDS_BASE + row * 256 + 16 * ((4 * db + u) ^ v_swz(row)) + 8 * (i & 1);
-    }
-    // K operand t (0..15) of the score product from K slot base kb (bytes): ks = t/2, block t%2.
-    auto k_operand = [&](uint32_t kb, int t) -> f16x8_t {
-        const int ks = t >> 1, mb = t & 1;
-        const uint32_t a = k_rd[ks] + kb + mb * 32 * 256;
-        return *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
-    };
-    // V operand of PV MFMA t (0..15) from V slot base vb: key chunk c = t/4, d block db = t%4.
-    auto v_operand = [&](uint32_t vb, int t) -> bf16x8_t {
-        const int c = t >> 2, db = t & 3;
-        const uint32_t a = v_rd[db] + vb + c * 16 * 256;
-        i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
-        i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 8 * 256));
-        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // Keys of tile j past the end of the sequence get -inf (only the last tile can have any).
-    auto mask_tail = [&](int j, f32x16_t (&s)[2]) {
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = j * BN + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                if (key >= seg_len) s[mb][i] = -INFINITY;
-            }
-    };
-    // Row max of a 64-key score tile (both lane halves).
-    auto row_max = [&](const f32x16_t (&s)[2]) -> float {
-        float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
-        mx = fmaxf(mx, s[0][15]);
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
-        return xhalf_max(mx);
-    };
-
-    f32x16_t oacc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
-    // Scores are in log2 units (q carries log2(e)/sqrt(D)).  m_run is the offset already taken
-    // off every score: the score MFMAs start from negm = -m_run instead of zero.
-    float m_run = 0.0f;
-    float l_run = 0.0f;
-    f32x16_t negm;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
-    const bool ragged = (seg_len % BN) != 0;
-    const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
-
-    // Scores of tile 0.
-    f32x16_t sa[2], sb[2];
-    {
-        f16x8_t ka[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) ka[t] = k_operand(0, t);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sa[mb][i] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 16; ++t)
-            sa[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sa[t & 1], 0, 0, 0);
-    }
-
-    // One tile step j (tile j in slot b): softmax weights and PV of tile j (scores sc) while the
-    // scores of tile j+1 (sn) are formed and tile j+PREF is fetched into slot (b+PREF) % NBUF.
-    auto step = [&](auto bufc, int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
-        constexpr int b = decltype(bufc)::value;
-        constexpr int b1 = (b + 1) % NBUF;
-        constexpr int bp = (b + PREF) % NBUF;
-        if (ragged && j == ntiles - 1) mask_tail(j, sc);
-        const float mx = row_max(sc);   // relative to m_run
-        // Lazy running max: move the offset only when this tile's max is well above it (and on
-        // the first tile, whose scores carry no offset yet).
-        const bool grow = (j == 0) | (mx > LAZY_LOG2);
-        if (__any(grow)) {
-            const float dm = grow ? mx : 0.0f;
-            const float alpha = j == 0 ? 1.0f : __builtin_amdgcn_exp2f(-dm);
-            m_run += dm;
-            l_run *= alpha;
+        for (int ks = 0; ks < 8; ++ks) k_rd[ks] = lds0 + l32 * 256 + 16 * ((2 * ks + hh) ^ k_swz(l32));
+        // V operand of the PV product, read transposed: lane (i = lane%16, g = lane/16) points at row
+        // 4*(g/2) + i/4 (+ 16 per key chunk, + 8 for the upper half) and channels 32 db + 16*(g%2) +
+        // 4*(i%4), i.e. logical chunk 4 db + 2*(g%2) + (i%4)/2, byte 8*(i%2) inside it.
+        uint32_t v_rd[4];
+        {
+            const int i = lane & 15, gq = lane >> 4;
+            const int row = 4 * (gq >> 1) + (i >> 2);
+            const int u = 2 * (gq & 1) + ((i & 3) >> 1);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                v_rd[db] = lds0 + V_LDS_BASE + row * 256 + 16 * ((4 * db + u) ^ v_swz(row)) + 8 * (i & 1);
+        }
+        // K operand t (0..15) of the score product from K slot base kb (bytes): ks = t/2, block t%2.
+        auto k_operand = [&](uint32_t kb, int t) -> f16x8_t {
+            const int ks = t >> 1, mb = t & 1;
+            const uint32_t a = k_rd[ks] + kb + mb * 32 * 256;
+            return *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
+        };
+        // V operand of PV MFMA t (0..15) from V slot base vb: key chunk c = t/4, d block db = t%4.
+        auto v_operand = [&](uint32_t vb, int t) -> bf16x8_t {
+            const int c = t >> 2, db = t & 3;
+            const uint32_t a = v_rd[db] + vb + c * 16 * 256;
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 8 * 256));
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // Keys of tile j past the end of the sequence get -inf (only the last tile can have any).
+        auto mask_tail = [&](int j, f32x16_t (&s)[2]) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sc[mb][i] -= dm;
+                for (int i = 0; i < 16; ++i) {
+                    const int key = j * BN + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
+                    if (key >= seg_len) s[mb][i] = -INFINITY;
+                }
+        };
+        // Row max of a 64-key score tile (both lane halves).
+        auto row_max = [&](const f32x16_t (&s)[2]) -> float {
+            float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) negm[i] = -m_run;
-        }
+            for (int i = 3; i < 15; i += 2) mx = fmaxf(fmaxf(mx, s[0][i]), s[0][i + 1]);
+            mx = fmaxf(mx, s[0][15]);
+#pragma unroll
+            for (int i = 0; i < 16; i += 2) mx = fmaxf(fmaxf(mx, s[1][i]), s[1][i + 1]);
+            return xhalf_max(mx);
+        };
 
-        // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
-        // last tile the K slot holds stale data and these scores are discarded.
-        f16x8_t ka[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t);
-        bf16x8_t pb[4];
-        float lpart[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int mb = c >> 1, o = 8 * (c & 1);
-            uint32_t u[4];
-            float ls = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e]);
-                const float p1 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e + 1]);
-                u[e] = pack_bf16x2(p0, p1);
-                ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
-                                                     __builtin_bit_cast(bf16x2_t, one2), ls, false);
-            }
-            lpart[c] = ls;
-            pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
-        }
-        l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
-        sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
-        sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
-#pragma unroll
-        for (int t = 2; t < 16; ++t)
-            sn[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sn[t & 1], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
-#pragma unroll
-        for (int t = 0; t < 12; ++t) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
-        }
-
-        // Fetch tile j+PREF into the slot read last before the previous barrier.  Past the last
-        // tile the fetch repeats the last tile into that free slot (nothing reads it again);
-        // issuing unconditionally keeps the count of copies in flight fixed.
-        issue_tile(min(j + PREF, ntiles - 1), bp);
-
-        // PV of tile j.
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const bf16x8_t va = v_operand(b * TILE_BYTES, t);
-            oacc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t >> 2], oacc[t & 3], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
-#pragma unroll
-        for (int t = 0; t < 13; ++t) {
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 0);
-
-        if constexpr (FUSED) {
-            finish_tile(min(j + PREF, ntiles - 1), bp);
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        } else {
-            // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
-            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
-        }
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
-
-    for (int j = 0; j < ntiles; j += 4) {
-        step(Buf<0>{}, j, sa, sb);
-        if (j + 1 >= ntiles) break;
-        step(Buf<1>{}, j + 1, sb, sa);
-        if (j + 2 >= ntiles) break;
-        step(Buf<2>{}, j + 2, sa, sb);
-        if (j + 3 >= ntiles) break;
-        step(Buf<3>{}, j + 3, sb, sa);
-    }
-    // Copies issued by the last steps (repeats of the last tile) must land before the
-    // workgroup's LDS is released.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-    // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
-    const float l_tot = xhalf_sum(l_run);
-    const float inv = 1.0f / l_tot;
-    if (p.lse && q_valid && hh == 0)
-        p.lse[(long long)q_row * p.heads + head] = m_run * 0.6931471805599453f + __logf(l_tot);
-    if (q_valid) {
-        uint16_t* op = p.out + q_row * row_stride + (long long)head * D;
+        f32x16_t oacc[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const int d0 = 32 * db + 8 * grp + 4 * hh;
-                uint2 u;
-                u.x = pack_bf16x2(oacc[db][4 * grp + 0] * inv, oacc[db][4 * grp + 1] * inv);
-                u.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
-                *reinterpret_cast<uint2*>(op + d0) = u;
+            for (int i = 0; i < 16; ++i) oacc[db][i] = 0.0f;
+        // Scores are in log2 units (q carries log2(e)/sqrt(D)).  m_run is the offset already taken
+        // off every score: the score MFMAs start from negm = -m_run instead of zero.
+        float m_run = 0.0f;
+        float l_run = 0.0f;
+        f32x16_t negm;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
+        const bool ragged = (seg_len % BN) != 0;
+        const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
+
+        // Scores of tile 0.
+        f32x16_t sa[2], sb[2];
+        {
+            f16x8_t ka[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) ka[t] = k_operand(0, t);
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sa[mb][i] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                sa[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sa[t & 1], 0, 0, 0);
+        }
+
+        // One tile step j (tile j in slot b): softmax weights and PV of tile j (scores sc) while the
+        // scores of tile j+1 (sn) are formed and tile j+PREF is fetched into slot (b+PREF) % NBUF.
+        auto step = [&](auto bufc, int j, f32x16_t (&sc)[2], f32x16_t (&sn)[2]) {
+            constexpr int b = decltype(bufc)::value;
+            constexpr int b1 = (b + 1) % NBUF;
+            constexpr int bp = (b + PREF) % NBUF;
+            if (ragged && j == ntiles - 1) mask_tail(j, sc);
+            const float mx = row_max(sc);   // relative to m_run
+            // Lazy running max: move the offset only when this tile's max is well above it (and on
+            // the first tile, whose scores carry no offset yet).
+            const bool grow = (j == 0) | (mx > LAZY_LOG2);
+            if (__any(grow)) {
+                const float dm = grow ? mx : 0.0f;
+                const float alpha = j == 0 ? 1.0f : __builtin_amdgcn_exp2f(-dm);
+                m_run += dm;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sc[mb][i] -= dm;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) negm[i] = -m_run;
             }
-    }
+
+            // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
+            // last tile the K slot holds stale data and these scores are discarded.
+            f16x8_t ka[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t);
+            bf16x8_t pb[4];
+            float lpart[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int mb = c >> 1, o = 8 * (c & 1);
+                uint32_t u[4];
+                float ls = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float p0 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e]);
+                    const float p1 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e + 1]);
+                    u[e] = pack_bf16x2(p0, p1);
+                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                         __builtin_bit_cast(bf16x2_t, one2), ls, false);
+                }
+                lpart[c] = ls;
+                pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
+            }
+            l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+            sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
+            sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
+#pragma unroll
+            for (int t = 2; t < 16; ++t)
+                sn[t & 1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[t], qreg[t >> 1], sn[t & 1], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+#pragma unroll
+            for (int t = 0; t < 12; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 5, 0);
+            }
+
+            // Fetch tile j+PREF into the slot read last before the previous barrier.  Past the last
+            // tile the fetch repeats the last tile into that free slot (nothing reads it again);
+            // issuing unconditionally keeps the count of copies in flight fixed.
+            issue_tile(min(j + PREF, ntiles - 1), bp);
+
+            // PV of tile j.
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const bf16x8_t va = v_operand(b * TILE_BYTES, t);
+                oacc[t & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[t >> 2], oacc[t & 3], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+#pragma unroll
+            for (int t = 0; t < 13; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 3, 0);
+
+            if constexpr (FUSED) {
+                finish_tile(min(j + PREF, ntiles - 1), bp);
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            } else {
+                // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
+                asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+
+        for (int j = 0; j < ntiles; j += 4) {
+            step(Buf<0>{}, j, sa, sb);
+            if (j + 1 >= ntiles) break;
+            step(Buf<1>{}, j + 1, sb, sa);
+            if (j + 2 >= ntiles) break;
+            step(Buf<2>{}, j + 2, sa, sb);
+            if (j + 3 >= ntiles) break;
+            step(Buf<3>{}, j + 3, sb, sa);
+        }
+        // Copies issued by the last steps (repeats of the last tile) must land before the
+        // workgroup's LDS is released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+        // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
+        const float l_tot = xhalf_sum(l_run);
+        const float inv = 1.0f / l_tot;
+        if (p.lse && q_valid && hh == 0)
+            p.lse[(long long)q_row * p.heads + head] = m_run * 0.6931471805599453f + __logf(l_tot);
+        if (q_valid) {
+            uint16_t* op = p.out + q_row * row_stride + (long long)head * D;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int grp = 0; grp < 4; ++grp) {
+                    const int d0 = 32 * db + 8 * grp + 4 * hh;
+                    uint2 u;
+                    u.x = pack_bf16x2(oacc[db][4 * grp + 0] * inv, oacc[db][4 * grp + 1] * inv);
+                    u.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
+                    *reinterpret_cast<uint2*>(op + d0) = u;
+                }
+        }
+    }  // item
 }
 
 // Staging for the default mode: one workgroup per (head, segment, key tile) rotates the tile's
@@ -580,10 +585,22 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 // cover all D/2 pairs (text rows read the position-0 entries).
 bool geom_covers_head(const RopeGeom& g) { return g.pairs[0] + g.pairs[1] + g.pairs[2] == D / 2; }
 
+// Workgroups of a persistent launch: one per CU (each holds 128 KB of LDS), rounded down to a
+// multiple of the 8 XCDs, and no more than there are items.
+int persistent_grid(int total) {
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
+        ncu = 256;
+    ncu -= ncu % 8;
+    return total < ncu ? total : ncu;
+}
+
 template <bool FUSED>
 hipError_t launch(const AttnParams& p, hipStream_t stream) {
     if (!geom_covers_head(p.g)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, false>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, false>), dim3(persistent_grid(p.total_wg)), dim3(NTHREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -642,7 +659,8 @@ hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uin
     if (!geom_covers_head(g)) return hipErrorInvalidValue;
     AttnParams p = make_params(q, kt, v, out, nullptr, table, g, heads, sl);
     p.win = m;
-    hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(p.total_wg), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(persistent_grid(p.total_wg)), dim3(NTHREADS), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
