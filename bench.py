@@ -212,7 +212,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel<false, false>",
+            "kernel": "attn_fwd_kernel<false, false, false>",
             "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -62,6 +62,7 @@ constexpr int NBUF = 4;                          // tile j lives in K and V slot
 constexpr int PREF = 3;                          // step j fetches tile j + PREF
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
+constexpr float OVF_SUM = 0x1p20f;   // fast launch: a tile weight sum this large flags the item
 constexpr float LAZY_LOG2 = 8.0f;  // move the offset when a row max exceeds it by more than this
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -91,6 +92,7 @@ struct AttnParams {
     int total_wg;
     float scale_log2;      // log2(e) / sqrt(D)
     WinMap win;            // window mode only: segment s is window s, rows via win_origin/offset
+    uint8_t* item_flags;   // 8 bytes per item: written by the fast launch, read by the guard launch
 };
 
 struct PrepParams {
@@ -154,15 +156,27 @@ constexpr int SG_DS_READ = 0x100;
 
 // WIN (staged K only): segment s is local window s of p.win, and query, value and output rows are
 // the window's grid rows (win_origin + win_offset) instead of a contiguous run of buffer rows.
-template <bool FUSED, bool WIN>
+// SAFE: the score offset follows the lazy running max of every tile (the row max of each tile is
+// formed).  !SAFE (the fast launch): the offset is the first tile's row max and is never moved;
+// when a tile's weight sum reaches OVF_SUM (or is not finite) the item is flagged, and a SAFE
+// guard launch on the same stream redoes exactly the flagged items.  Without a rescale the
+// weights of a row stay below OVF_SUM = 2^20 in the fast launch, so its accumulator is at most
+// 2^12 times larger than with the running max.
+template <bool FUSED, bool WIN, bool SAFE>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     static_assert(!(FUSED && WIN), "window mode reads staged K");
+    static_assert(SAFE || !FUSED, "the fused variant always tracks the running max");
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
     // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
     for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
+        if constexpr (SAFE) {
+            // Guard launch: only the items the fast launch flagged.
+            if (p.item_flags && *reinterpret_cast<const unsigned long long*>(p.item_flags + 8ll * item) == 0)
+                continue;
+        }
         const int logical = xcd_remap(item, p.total_wg);
         const int qt = logical % p.q_tiles;
         const int rest = logical / p.q_tiles;
@@ -372,6 +386,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         // off every score: the score MFMAs start from negm = -m_run instead of zero.
         float m_run = 0.0f;
         float l_run = 0.0f;
+        bool ovf = false;   // fast launch: this lane saw a tile weight sum of OVF_SUM or more
         f32x16_t negm;
 #pragma unroll
         for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
@@ -400,25 +415,27 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             constexpr int b1 = (b + 1) % NBUF;
             constexpr int bp = (b + PREF) % NBUF;
             if (ragged && j == ntiles - 1) mask_tail(j, sc);
-            const float mx = row_max(sc);   // relative to m_run
-            // Lazy running max: move the offset only when this tile's max is well above it (and on
-            // the first tile, whose scores carry no offset yet).
-            const bool grow = (j == 0) | (mx > LAZY_LOG2);
-            if (__any(grow)) {
-                const float dm = grow ? mx : 0.0f;
-                const float alpha = j == 0 ? 1.0f : __builtin_amdgcn_exp2f(-dm);
-                m_run += dm;
-                l_run *= alpha;
+            if (SAFE || j == 0) {
+                const float mx = row_max(sc);   // relative to m_run
+                // Lazy running max: move the offset only when this tile's max is well above it (and on
+                // the first tile, whose scores carry no offset yet).
+                const bool grow = (j == 0) | (mx > LAZY_LOG2);
+                if (__any(grow)) {
+                    const float dm = grow ? mx : 0.0f;
+                    const float alpha = j == 0 ? 1.0f : __builtin_amdgcn_exp2f(-dm);
+                    m_run += dm;
+                    l_run *= alpha;
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                    for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+                        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sc[mb][i] -= dm;
+                        for (int i = 0; i < 16; ++i) sc[mb][i] -= dm;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) negm[i] = -m_run;
+                    for (int i = 0; i < 16; ++i) negm[i] = -m_run;
+                }
             }
 
             // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
@@ -444,7 +461,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                 lpart[c] = ls;
                 pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
             }
-            l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+            {
+                const float lt = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+                l_run += lt;
+                if constexpr (!SAFE) ovf |= !(lt < OVF_SUM);
+            }
             sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
             sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
 #pragma unroll
@@ -505,6 +526,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         // Copies issued by the last steps (repeats of the last tile) must land before the
         // workgroup's LDS is released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+        if constexpr (!SAFE) {
+            const bool flagged = __any(ovf);
+            if (lane == 0) p.item_flags[8ll * item + wave] = flagged ? 1 : 0;
+        }
 
         // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
         const float l_tot = xhalf_sum(l_run);
@@ -578,6 +604,7 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     p.total_wg = p.q_tiles * L.n_segs * heads;
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     p.win = WinMap{};
+    p.item_flags = nullptr;
     return p;
 }
 
@@ -596,11 +623,28 @@ int persistent_grid(int total) {
     return total < ncu ? total : ncu;
 }
 
-template <bool FUSED>
-hipError_t launch(const AttnParams& p, hipStream_t stream) {
+// The fast launch pays a second (guard) launch; below this many (item, key tile) pairs the safe
+// kernel alone is quicker.
+constexpr long long kFastMinTiles = 32768;
+
+// Staged (FUSED = false) launches: with `flags` (8 bytes per item, attn_flag_bytes), the fast
+// kernel followed by the guard launch of the safe kernel; otherwise the safe kernel alone.
+template <bool FUSED, bool WIN>
+hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
     if (!geom_covers_head(p.g)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, false>), dim3(persistent_grid(p.total_wg)), dim3(NTHREADS), 0,
-                       stream, p);
+    const dim3 grid(persistent_grid(p.total_wg));
+    if constexpr (!FUSED) {
+        if (flags && (long long)p.total_wg * p.k_tiles >= kFastMinTiles) {
+            p.item_flags = flags;
+            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN, false>), grid, dim3(NTHREADS), 0, stream, p);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN, true>), grid, dim3(NTHREADS), 0, stream, p);
+            return hipGetLastError();
+        }
+    }
+    p.item_flags = nullptr;
+    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, WIN, true>), grid, dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -609,6 +653,10 @@ hipError_t launch(const AttnParams& p, hipStream_t stream) {
 size_t attn_stage_elems(int heads, int kv_len, int n_segs) {
     const size_t k_tiles = (size_t)(kv_len + BN - 1) / BN;
     return (size_t)heads * n_segs * k_tiles * BN * D;
+}
+
+size_t attn_flag_bytes(int heads, int q_len, int n_segs) {
+    return (size_t)((q_len + BM - 1) / BM) * n_segs * heads * 8;
 }
 
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
@@ -649,33 +697,31 @@ hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* tabl
 
 hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                 uint16_t* out, const float2* table, const RopeGeom& g, int heads,
-                                const WinMap& m, int n_windows, int L, hipStream_t stream) {
+                                const WinMap& m, int n_windows, int L, uint8_t* flags,
+                                hipStream_t stream) {
     SeqLayout sl;
     sl.n_segs = n_windows;
     sl.q_len = L;
     sl.kv_len = L;
     sl.q_pos_base = 0;
     sl.kv_pos_base = 0;
-    if (!geom_covers_head(g)) return hipErrorInvalidValue;
     AttnParams p = make_params(q, kt, v, out, nullptr, table, g, heads, sl);
     p.win = m;
-    hipLaunchKernelGGL((attn_fwd_kernel<false, true>), dim3(persistent_grid(p.total_wg)), dim3(NTHREADS), 0,
-                       stream, p);
-    return hipGetLastError();
+    return launch<false, true>(p, flags, stream);
 }
 
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, float* lse, const float2* table,
-                                   const RopeGeom& g, int heads, const SeqLayout& L,
+                                   const RopeGeom& g, int heads, const SeqLayout& L, uint8_t* flags,
                                    hipStream_t stream) {
-    return launch<false>(make_params(q, kt, v, out, lse, table, g, heads, L), stream);
+    return launch<false, false>(make_params(q, kt, v, out, lse, table, g, heads, L), flags, stream);
 }
 
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* out, float* lse, const float2* table,
                                   const RopeGeom& g, int heads, const SeqLayout& L,
                                   hipStream_t stream) {
-    return launch<true>(make_params(q, k, v, out, lse, table, g, heads, L), stream);
+    return launch<true, false>(make_params(q, k, v, out, lse, table, g, heads, L), nullptr, stream);
 }
 
 }  // namespace st

@@ -166,18 +166,24 @@ st_status hip_fail(hipError_t e) {
     return ST_ERR_HIP;
 }
 
-// Byte layout of the bf16 staged workspace: [table][K~ tiles], each 256-aligned.
+// Byte layout of the bf16 staged workspace: [table][K~ tiles][item flags], each 256-aligned.  The
+// flags (8 bytes per 256-row query block of each sequence and head) are scratch of the attention
+// launches; sequences are self-attention ones (query rows = key rows = seg_len).
 struct StageLayout {
     size_t table_bytes;
     size_t tiles_bytes;
+    size_t flags_bytes;
     size_t total;
+    size_t flags_offset() const { return table_bytes + tiles_bytes; }
 };
 
-StageLayout stage_layout(int T, int H, int W, int heads, int seg_len, int n_segs, const int* split) {
+StageLayout stage_layout(int T, int H, int W, int heads, int seg_len, int n_segs, const int* split,
+                         bool with_flags = true) {
     StageLayout L;
     L.table_bytes = table_bytes_for(T, H, W, split);
     L.tiles_bytes = align_up(st::attn_stage_elems(heads, seg_len, n_segs) * 2, kWsAlign);
-    L.total = L.table_bytes + L.tiles_bytes;
+    L.flags_bytes = with_flags ? align_up(st::attn_flag_bytes(heads, seg_len, n_segs), kWsAlign) : 0;
+    L.total = L.table_bytes + L.tiles_bytes + L.flags_bytes;
     return L;
 }
 
@@ -254,7 +260,7 @@ st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int he
 }
 
 st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, int n_text, int heads,
-                           int d, const int rope_split[3], st_dtype dtype, const void* workspace,
+                           int d, const int rope_split[3], st_dtype dtype, void* workspace,
                            size_t ws_bytes, void* out, hipStream_t stream) {
     long long n = 0;
     if (!workspace) return ST_ERR_NULL;
@@ -267,10 +273,11 @@ st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, in
     if (ws_overlaps_tensors(workspace, ws_bytes, (size_t)n * heads * d * 2, q, v, out, nullptr))
         return ST_ERR_ALIAS;
     st::RopeGeom g = st::make_geom(T, H, W, rope_split);
-    const char* ws = (const char*)workspace;
+    char* ws = (char*)workspace;
     hipError_t e = st::launch_attn_bf16_staged((const uint16_t*)q, (const uint16_t*)(ws + L.table_bytes),
                                                (const uint16_t*)v, (uint16_t*)out, nullptr,
-                                               (const float2*)ws, g, heads, self_layout((int)n), stream);
+                                               (const float2*)ws, g, heads, self_layout((int)n),
+                                               (uint8_t*)(ws + L.flags_offset()), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
 }
 
@@ -378,7 +385,7 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, SL, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, o_s, nullptr, table,
-                                        g, heads, SL, stream);
+                                        g, heads, SL, (uint8_t*)(ws + L.flags_offset()), stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_temporal_bf16((const uint16_t*)q, (const uint16_t*)k, kt, o_s,
                                           (uint16_t*)out, table, g, heads, stream);
@@ -444,7 +451,7 @@ st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int 
         e = st::launch_k_prep_win((const uint16_t*)k, kt, table, g, heads, m, n_win, L, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_bf16_win((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out, table, g,
-                                     heads, m, n_win, L, stream);
+                                     heads, m, n_win, L, (uint8_t*)(ws + SL.flags_offset()), stream);
     } else {
         st::F32Layout FL = f32_layout(n_win, L, 0, 1, L, 0, 1);
         FL.win = 1;
@@ -547,7 +554,7 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out,
-                                        nullptr, table, g, heads, L, stream);
+                                        nullptr, table, g, heads, L, nullptr, stream);
     } else {
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
                                 table, g, heads, d, f32_layout(1, n_q, 0, 1, n_kv, 0, 1), stream);
@@ -626,7 +633,8 @@ size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int he
     if (kv_count < 1 || kv_count > n) return 0;
     if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) : 0;
     if (dtype != ST_BF16 || d != 128) return 0;
-    return stage_layout(T, H, W, heads, kv_count, 1, rope_split).total;
+    // Partial results run the running-max kernel alone: no block flags.
+    return stage_layout(T, H, W, heads, kv_count, 1, rope_split, false).total;
 }
 
 st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
@@ -684,7 +692,7 @@ st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
         if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out, lse,
-                                        table, g, heads, L, stream);
+                                        table, g, heads, L, nullptr, stream);
     } else {
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
                                 table, g, heads, d,

@@ -181,19 +181,23 @@ hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* tabl
                              int heads, const WinMap& m, int n_windows, int L, hipStream_t stream);
 hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                 uint16_t* out, const float2* table, const RopeGeom& g, int heads,
-                                const WinMap& m, int n_windows, int L, hipStream_t stream);
+                                const WinMap& m, int n_windows, int L, uint8_t* flags,
+                                hipStream_t stream);
 
 // Flash attention for bf16 storage, d = 128.
 // Staged mode: launch_k_prep rotates K into fp16 tiles `kt` (attn_stage_elems(...) uint16
 // elements), then launch_attn_bf16_staged reads them together with V.
 // Fused mode: launch_attn_bf16_fused reads K directly and rotates it on every tile load.
 // `lse`, when not null, receives [q rows][heads] log-sum-exp of the scaled scores.
+// `flags` (attn_flag_bytes(heads, q_len, n_segs) bytes of device memory, or null): scratch of the
+// fast launch and its guard launch; with null only the kernel that tracks the running max runs.
 size_t attn_stage_elems(int heads, int kv_len, int n_segs);
+size_t attn_flag_bytes(int heads, int q_len, int n_segs);
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
                          int heads, const SeqLayout& L, hipStream_t stream);
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, float* lse, const float2* table,
-                                   const RopeGeom& g, int heads, const SeqLayout& L,
+                                   const RopeGeom& g, int heads, const SeqLayout& L, uint8_t* flags,
                                    hipStream_t stream);
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* out, float* lse, const float2* table,

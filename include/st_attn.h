@@ -89,7 +89,11 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  *   stage:  the angle table and the rotated K rows as fp16 tiles of 64 keys, written into the
  *           caller's workspace (one pass over K);
  *   attend: the attention kernel; it rotates Q itself and streams the staged K tiles and the
- *           caller's V.
+ *           caller's V.  It runs in two launches: the first takes each row's score offset from
+ *           its first 64 keys only and flags any block of 256 query rows whose softmax weights
+ *           reach 2^20 (or are not finite) in the workspace; the second redoes only flagged
+ *           blocks with a running maximum over every 64 keys.  Attention over fewer than 32768
+ *           (block, 64-key tile) pairs runs the second kind alone.
  * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
  * fp16 for the score product, so every rotated q/k entry must stay below 65504 in magnitude
  * (inputs with |x| < 2^15 are always safe); softmax weights multiply V in bf16.
@@ -97,8 +101,8 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  * ------------------------------------------------------------------------------------------- */
 
 /* Workspace bytes st_attn3d_fwd (and stage/attend) need; 0 if the arguments are invalid.
- * ST_BF16: table + heads x ceil(N/64) x 64 x d x 2 bytes (256-byte aligned parts); ST_F32:
- * table. */
+ * ST_BF16: table + heads x ceil(N/64) x 64 x d x 2 bytes (K tiles) + heads x ceil(N/256) x 8
+ * bytes (block flags), each part 256-byte aligned; ST_F32: table. */
 size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
                                  const int rope_split[3], st_dtype dtype);
 
@@ -116,11 +120,12 @@ st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int he
                           void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Second step of the ST_BF16 path: attention of q against the K tiles st_attn3d_stage wrote
- * for the same grid, n_text, heads, d and rope_split (read only), with values v.  One kernel
- * launch. */
+ * for the same grid, n_text, heads, d and rope_split (read only), with values v.  The block-flag
+ * part of the workspace is written (scratch), so calls sharing one workspace must not overlap.
+ * Two kernel launches (see above). */
 st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, int n_text,
                            int heads, int d, const int rope_split[3], st_dtype dtype,
-                           const void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
+                           void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* Workspace bytes of st_attn3d_fwd_fused: the angle table only. */
 size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split[3]);
@@ -142,7 +147,7 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
  * ------------------------------------------------------------------------------------------- */
 
 /* Workspace bytes: the angle table, for ST_BF16 the staged K tiles of the per-frame sequences
- * (as for st_attn3d_fwd), and the stage-1 output [N][heads][d] of `dtype`. */
+ * and their block flags (as for st_attn3d_fwd), and the stage-1 output [N][heads][d] of `dtype`. */
 size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
                                           const int rope_split[3], st_dtype dtype);
 
@@ -164,8 +169,8 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v,
  * ST_BF16: d == 128, numerics as st_attn3d_fwd, N*heads*d*2 bytes below 2^32 (else
  * ST_ERR_UNSUPPORTED).  ST_F32: even d <= 128, at most 65535 windows.  Workspace (caller-owned,
  * 256-byte aligned, st_attn3d_window_workspace_bytes bytes, 0 for an invalid request): the angle
- * table and, for bf16, the rotated fp16 key tiles of every window.  Three launches (table, key
- * staging, attention) on `stream`.
+ * table and, for bf16, the rotated fp16 key tiles and the block flags of every window.  Three or
+ * four launches (table, key staging, attention as in st_attn3d_attend) on `stream`.
  * ------------------------------------------------------------------------------------------- */
 size_t st_attn3d_window_workspace_bytes(int T, int H, int W, int heads, int d,
                                         const int rope_split[3], const int window[3],

@@ -78,12 +78,14 @@ def test_table_bytes(lib):
 
 
 def test_attn3d_workspace_bytes(lib):
-    # bf16: table + rotated-K tiles of 64 keys x 128 channels x 2 bytes
+    # bf16: table + rotated-K tiles of 64 keys x 128 channels x 2 bytes + 8 flag bytes per
+    # 256-row query block and head
     for (t, h, w), n_text, heads in [((21, 30, 52), 0, 12), ((33, 45, 80), 256, 24), ((1, 1, 1), 0, 1)]:
         n = t * h * w + n_text
         tb = lib.st_rope3d_table_bytes(t, h, w, sp(44, 42, 42))
         tiles = ((heads * ((n + 63) // 64) * 64 * 128 * 2) + 255) // 256 * 256
-        assert lib.st_attn3d_workspace_bytes(t, h, w, n_text, heads, 128, sp(44, 42, 42), 0) == tb + tiles
+        flags = (heads * ((n + 255) // 256) * 8 + 255) // 256 * 256
+        assert lib.st_attn3d_workspace_bytes(t, h, w, n_text, heads, 128, sp(44, 42, 42), 0) == tb + tiles + flags
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, 0, 2, 64, sp(20, 22, 22), 0) == 0   # bf16 d != 128
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, 0, 0, 128, sp(44, 42, 42), 0) == 0
     assert lib.st_attn3d_workspace_bytes(3, 4, 6, -1, 2, 128, sp(44, 42, 42), 0) == 0
@@ -94,8 +96,9 @@ def test_factorized_workspace_bytes(lib):
     tb = lib.st_rope3d_table_bytes(21, 30, 52, sp(44, 42, 42))
     n = 21 * 30 * 52
     tiles = (12 * 21 * ((1560 + 63) // 64) * 64 * 128 * 2 + 255) // 256 * 256
+    flags = (12 * 21 * ((1560 + 255) // 256) * 8 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 0) == \
-        tb + tiles + (n * 12 * 128 * 2 + 255) // 256 * 256
+        tb + tiles + flags + (n * 12 * 128 * 2 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), 1) == \
         tb + (n * 12 * 128 * 4 + 255) // 256 * 256
     assert lib.st_attn_factorized_workspace_bytes(21, 30, 52, 0, 128, sp(44, 42, 42), 0) == 0
@@ -366,8 +369,9 @@ def test_window_workspace_bytes(lib):
     tb = lib.st_rope3d_table_bytes(21, 30, 52, sp(44, 42, 42))
     # 36 windows of 7 x 10 x 13 = 910 tokens: 15 key tiles of 64 rows each per window and head
     tiles = (12 * 36 * 15 * 64 * 128 * 2 + 255) // 256 * 256
+    flags = (12 * 36 * 4 * 8 + 255) // 256 * 256          # 4 query blocks of 256 rows per window
     assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 13), 0) == \
-        tb + tiles
+        tb + tiles + flags
     assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 13), 1) == tb
     assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(7, 10, 12), 0) == 0
     assert lib.st_attn3d_window_workspace_bytes(21, 30, 52, 12, 128, sp(44, 42, 42), win(0, 10, 13), 0) == 0

@@ -167,6 +167,49 @@ def test_running_max_keeps_growing(dtype):
         assert rel <= 5e-3 and max_abs <= 5e-2
 
 
+# The attend step runs a fast kernel (score offset from each row's first 64 keys, never moved)
+# and a guard launch that redoes, with the running-max kernel, every 256-row block whose weights
+# reached 2^20.  It does so from 32768 (block, 64-key tile) pairs up; 16384 tokens x 2 heads is
+# the smallest grid of that size.  The partial-attention entry point runs the running-max kernel
+# alone over the same rows.
+FAST_GRID = (8, 32, 64)
+
+
+def test_fast_launch_equals_running_max_kernel_bitwise():
+    """N(0,1) inputs never move a row's maximum by more than 8 after the first tile, so the fast
+    launch and the running-max kernel do the same arithmetic."""
+    n = 8 * 32 * 64
+    log(f"  fast launch vs running-max kernel grid={FAST_GRID} heads=2 dtype=bf16 seed=330")
+    x = make_qkv(n, 2, 128, 330, "bf16")
+    q, k, v = to_device(x)
+    fast = fa.attn3d(q, k, v, FAST_GRID)
+    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
+    torch.cuda.synchronize()
+    assert torch.equal(fast.view(torch.int16), safe.view(torch.int16))
+
+
+@pytest.mark.parametrize("q_mult,k_ramp", [(2.0, 1.5), (6.0, 3.0)])
+def test_fast_launch_redoes_blocks_whose_weights_grow(q_mult, k_ramp):
+    """Keys whose norm grows along the sequence: later tiles score far above the first one, the
+    fast launch flags those blocks (weights past 2^20, or infinite) and the guard redoes them."""
+    n = 8 * 32 * 64
+    rows = sample_rows(n, n, 2048, 384, 331)
+    got, ref = run_full(FAST_GRID, 2, "bf16", 331, rows=rows, q_mult=q_mult, k_ramp=k_ramp)
+    assert np.isfinite(got).all()
+    max_abs, rel = errors(got, ref)
+    log(f"    fast launch, growing maximum q_mult={q_mult} k_ramp={k_ramp}: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    # bounds as in test_running_max_keeps_growing (scores of |s| ~ 100 in log2 units)
+    assert rel <= 5e-3 and max_abs <= 5e-2
+    # and the same rows from the running-max kernel alone agree to the same bound
+    x = make_qkv(n, 2, 128, 331, "bf16", q_mult=q_mult, k_ramp=k_ramp)
+    q, k, v = to_device(x)
+    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
+    torch.cuda.synchronize()
+    m2, r2 = errors(got, host_f64(safe)[rows])
+    log(f"    fast launch vs running-max kernel: max_abs={m2:.3e} rel_l2={r2:.3e}")
+    assert r2 <= 5e-3 and m2 <= 5e-2
+
+
 def test_stage_attend_matches_fwd_bitwise():
     grid, heads = (5, 9, 11), 2
     x = make_qkv(495, heads, 128, 400, "bf16")
