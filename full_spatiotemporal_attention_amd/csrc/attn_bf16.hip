@@ -62,7 +62,7 @@ constexpr int NBUF = 4;                          // tile j lives in K and V slot
 constexpr int PREF = 3;                          // step j fetches tile j + PREF
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
-constexpr float OVF_SUM = 0x1p20f;   // fast launch: a tile weight sum this large flags the item
+constexpr float OVF_SUM = 0x1p64f;   // fast launch: a row sum this large (or not finite) flags the item
 constexpr float LAZY_LOG2 = 8.0f;  // move the offset when a row max exceeds it by more than this
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -157,11 +157,10 @@ constexpr int SG_DS_READ = 0x100;
 // WIN (staged K only): segment s is local window s of p.win, and query, value and output rows are
 // the window's grid rows (win_origin + win_offset) instead of a contiguous run of buffer rows.
 // SAFE: the score offset follows the lazy running max of every tile (the row max of each tile is
-// formed).  !SAFE (the fast launch): the offset is the first tile's row max and is never moved;
-// when a tile's weight sum reaches OVF_SUM (or is not finite) the item is flagged, and a SAFE
-// guard launch on the same stream redoes exactly the flagged items.  Without a rescale the
-// weights of a row stay below OVF_SUM = 2^20 in the fast launch, so its accumulator is at most
-// 2^12 times larger than with the running max.
+// formed).  !SAFE (the fast launch): the offset is the first tile's row max and is never moved, so
+// a row's sum only grows and bounds every weight it has used; an item whose row sum reaches
+// OVF_SUM = 2^64 (or is not finite) is flagged, and a SAFE guard launch on the same stream redoes
+// exactly the flagged items.  Unflagged, the accumulator stays below 2^64 |v|.
 template <bool FUSED, bool WIN, bool SAFE>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     static_assert(!(FUSED && WIN), "window mode reads staged K");
@@ -204,11 +203,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
         uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
         int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
+        uint32_t vch2[2];        // the same in bytes
+        const uint32_t rs2 = 2u * (uint32_t)row_stride;   // bytes per V row (< 2^24)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = dr0 + 4 * i;
             k_src_off[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ k_swz(r)));
             v_chunk[i] = 8 * (pc ^ v_swz(r));
+            vch2[i] = 2u * (uint32_t)v_chunk[i];
         }
         // FUSED K copy through registers: thread owns chunks c = tid & 15 of rows tid>>4 and +32.
         const int fkc = tid & 15;
@@ -235,7 +237,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                 for (int i = 0; i < 2; ++i) {
                     const int r = dr0 + 4 * i;
                     const int re = r < last ? r : last;
-                    dma16(vt, 2u * (uint32_t)(re * (int)row_stride + v_chunk[i]), vl + i * 1024);
+                    dma16(vt, __umul24((uint32_t)re, rs2) + vch2[i], vl + i * 1024);
                 }
             }
             if constexpr (!FUSED) {
@@ -386,7 +388,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         // off every score: the score MFMAs start from negm = -m_run instead of zero.
         float m_run = 0.0f;
         float l_run = 0.0f;
-        bool ovf = false;   // fast launch: this lane saw a tile weight sum of OVF_SUM or more
         f32x16_t negm;
 #pragma unroll
         for (int i = 0; i < 16; ++i) negm[i] = 0.0f;
@@ -461,11 +462,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                 lpart[c] = ls;
                 pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
             }
-            {
-                const float lt = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
-                l_run += lt;
-                if constexpr (!SAFE) ovf |= !(lt < OVF_SUM);
-            }
+            l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
             sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
             sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
 #pragma unroll
@@ -528,7 +525,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
         if constexpr (!SAFE) {
-            const bool flagged = __any(ovf);
+            // The fast launch never rescales, so the row sum bounds every weight it has used.
+            const bool flagged = __any(!(l_run < OVF_SUM));
             if (lane == 0) p.item_flags[8ll * item + wave] = flagged ? 1 : 0;
         }
 
