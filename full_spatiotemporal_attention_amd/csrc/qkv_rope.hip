@@ -175,14 +175,39 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
     // Lane (l32, hh) holds, for block (fb, tb), token 128 tg + 32 tb + l32 and features
     // 64 fg + 32 fb + 8 (i / 4) + 4 hh + i % 4 of the tile.
     const RopeGeom& g = p.g;
+    // The lane's 32 features are the same for all four token blocks: their bias is loaded once.
+    // Table entries of token block tb + 1 are loaded while block tb is rotated and stored.
+    const bool has_bias = p.bias != nullptr;
+    uint2 bw[2][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-        __builtin_amdgcn_sched_barrier(0);            // one token block at a time (register use)
-        const int row = 128 * tg + 32 * tb + l32;     // token row inside the tile
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int f = f0 + 64 * fg + 32 * fb + 8 * gi + 4 * hh;
+            bw[fb][gi] = (has_bias && f < F) ? *reinterpret_cast<const uint2*>(p.bias + f) : make_uint2(0u, 0u);
+        }
+    // Pair entries of token block tb for the q and k features of this lane (v features: unused).
+    auto load_cs = [&](int tb, float2 (&cs)[2][4][2]) {
+        const int row = 128 * tg + 32 * tb + l32;
         const int n = min(m0 + row, p.n_rows - 1);
         int t = 0, h = 0, w = 0;
         const bool text = n >= g.Nv;
         if (!text) decode_pos(n, g, t, h, w);
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int f = f0 + 64 * fg + 32 * fb + 8 * gi + 4 * hh;
+                const int pair = (f % 128) >> 1;
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    cs[fb][gi][e] = f < 2 * C ? p.table[pair_entry(pair + e, t, h, w, text, g)]
+                                              : make_float2(1.0f, 0.0f);
+            }
+    };
+    float2 csa[2][4][2], csb[2][4][2];
+    auto block = [&](int tb, const float2 (&cs)[2][4][2]) {
+        const int row = 128 * tg + 32 * tb + l32;     // token row inside the tile
 #pragma unroll
         for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
@@ -192,26 +217,27 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
                 float y[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][4 * gi + e];
-                if (p.bias && f < F) {
-                    const uint2 bw = *reinterpret_cast<const uint2*>(p.bias + f);
-                    y[0] += bf16_lo(bw.x);
-                    y[1] += bf16_hi(bw.x);
-                    y[2] += bf16_lo(bw.y);
-                    y[3] += bf16_hi(bw.y);
-                }
+                y[0] += bf16_lo(bw[fb][gi].x);
+                y[1] += bf16_hi(bw[fb][gi].x);
+                y[2] += bf16_lo(bw[fb][gi].y);
+                y[3] += bf16_hi(bw[fb][gi].y);
                 if (f < 2 * C) {                  // q or k: rotate pairs (f, f+1), (f+2, f+3)
-                    const int pair = (f % 128) >> 1;
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float2 cs = p.table[pair_entry(pair + e, t, h, w, text, g)];
-                        rotate_pair(y[2 * e], y[2 * e + 1], cs);
-                    }
+                    for (int e = 0; e < 2; ++e) rotate_pair(y[2 * e], y[2 * e + 1], cs[fb][gi][e]);
                 }
                 const u32x2_t pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
                 const uint32_t a = lds0 + row * 512 + 16 * ((fl >> 3) ^ (row & 31)) + 8 * hh;
                 *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)a = pk;
             }
-    }
+    };
+    load_cs(0, csa);
+    load_cs(1, csb);
+    block(0, csa);
+    load_cs(2, csa);
+    block(1, csb);
+    load_cs(3, csb);
+    block(2, csa);
+    block(3, csb);
     __syncthreads();
     // Wave w writes tile rows 32 w .. +31, two rows (2 x 512 bytes) per store.
 #pragma unroll 4
