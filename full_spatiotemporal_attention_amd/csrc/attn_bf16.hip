@@ -219,8 +219,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 
         // issue_tile(j, slot): fetch tile j into K and V slot `slot`.
         auto issue_tile = [&](int j, int slot) {
-            const uint32_t kl = lds0 + slot * TILE_BYTES + (8 * wave) * 256;
-            const uint32_t vl = lds0 + V_LDS_BASE + slot * TILE_BYTES + (8 * wave) * 256;
+            // The wave's LDS base passes through an empty asm so that the copies' LDS addresses are
+            // formed here by scalar adds; hoisted out of the loop, their 16 values were spilled and
+            // reloaded with VALU lane reads on every tile.
+            uint32_t wl = lds0 + (8 * wave) * 256;
+            asm volatile("" : "+s"(wl));
+            const uint32_t kl = wl + slot * TILE_BYTES;
+            const uint32_t vl = wl + V_LDS_BASE + slot * TILE_BYTES;
             const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
             if constexpr (WIN) {
                 // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
@@ -359,14 +364,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         // Keys of tile j past the end of the sequence get -inf (only the last tile can have any).
+        // The limit passes through an empty asm so that its 32 compares stay in this rarely taken
+        // branch: hoisted out of the loop they held 64 SGPRs and pushed other values into spills.
         auto mask_tail = [&](int j, f32x16_t (&s)[2]) {
+            int lim = seg_len - j * BN - 4 * hh;   // first key offset in the tile past the end
+            asm volatile("" : "+v"(lim));
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = j * BN + 32 * mb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key >= seg_len) s[mb][i] = -INFINITY;
-                }
+                for (int i = 0; i < 16; ++i)
+                    if (32 * mb + 8 * (i >> 2) + (i & 3) >= lim) s[mb][i] = -INFINITY;
         };
         // Row max of a 64-key score tile (both lane halves).
         auto row_max = [&](const f32x16_t (&s)[2]) -> float {
@@ -444,25 +451,28 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             f16x8_t ka[16];
 #pragma unroll
             for (int t = 0; t < 16; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t);
+            // The rounded weights are summed in two chains, one of them the running row sum.
             bf16x8_t pb[4];
-            float lpart[4];
+            float l2 = 0.0f;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int mb = c >> 1, o = 8 * (c & 1);
                 uint32_t u[4];
-                float ls = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float p0 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e]);
                     const float p1 = __builtin_amdgcn_exp2f(sc[mb][o + 2 * e + 1]);
                     u[e] = pack_bf16x2(p0, p1);
-                    ls = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
-                                                         __builtin_bit_cast(bf16x2_t, one2), ls, false);
+                    if (c & 1)
+                        l2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                             __builtin_bit_cast(bf16x2_t, one2), l2, false);
+                    else
+                        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                                __builtin_bit_cast(bf16x2_t, one2), l_run, false);
                 }
-                lpart[c] = ls;
                 pb[c] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
             }
-            l_run += (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+            l_run += l2;
             sn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[0], qreg[0], negm, 0, 0, 0);
             sn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[1], qreg[0], negm, 0, 0, 0);
 #pragma unroll
