@@ -33,7 +33,7 @@ THETA = 10000.0
 SEED = 2000
 BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_kernel_wan13b_81f_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fast_kernel_wan13b_81f_traffic.txt")
 COPY_BYTES = 256 << 20       # device copy timed under the counters to scale FETCH_SIZE/WRITE_SIZE
 KERNEL_SOURCES = ["full_spatiotemporal_attention_amd/csrc/attn_bf16.hip",
                   "full_spatiotemporal_attention_amd/csrc/st_internal.h"]
@@ -212,7 +212,7 @@ def main():
         "pct_of_bf16_peak": round(100.0 * value / BF16_PEAK_TFLOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_kernel<false, false, false>",
+            "kernel": "attn_fast_kernel<false>",
             "achieved": round(achieved, 2),
             "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -8,10 +8,12 @@
 // of one frame (the spatial stage of factorised attention, "How attention sees time").
 //
 // Numerics: rotated q and k are rounded once to fp16 (11 significant bits) for the score product
-// (v_mfma_f32_32x32x16_f16, same rate as bf16); q is multiplied by log2(e)/sqrt(128) before that
-// rounding, so scores come out in log2 units.  Softmax weights are rounded to bf16 and multiply
-// the exact bf16 values (v_mfma_f32_32x32x16_bf16); accumulation, the running max and the row
-// sums are fp32, and the row sum adds exactly the rounded weights the product used.
+// (f16 MFMAs, same rate as bf16); q is multiplied by log2(e)/sqrt(128) before that rounding, so
+// scores come out in log2 units.  Softmax weights are rounded to bf16 and multiply the exact bf16
+// values (bf16 MFMAs); accumulation, the running max and the row sums are fp32, and the row sum
+// adds exactly the rounded weights the product used.  (bf16 q and k would make the score product
+// cheaper, but their rounding alone takes the Wan-14B-shaped 720p inputs, whose rows are scaled
+// by U(0.5, 2), past a relative L2 error of 5e-3.)
 //
 // How K reaches the kernel (template flag FUSED):
 //  * staged (default): a preparation kernel rotates K once per key into fp16 tiles
@@ -27,18 +29,21 @@
 // kernel does the same for K.
 //
 // Design (one item = 256 query rows of one head and one sequence, taken by a workgroup of 8 waves;
-// the launch is persistent: one workgroup per CU loops over items):
-//  * Scores are formed transposed, S^T = K~ Q~^T: a lane owns one query column and 16 keys per
-//    32x32 block, so the softmax row max and row sum are in-lane plus one exchange between the
-//    two 32-lane halves (v_permlane32_swap).
+// the launch is persistent: one workgroup per CU loops over items).  Two kernels share it: the
+// fast launch (attn_fast_kernel, 16x16x32 blocks, fixed score offset) and the running-max kernel
+// (attn_fwd_kernel, 32x32x16 blocks), which is the guard of the fast launch and serves every
+// other path.
+//  * Scores are formed transposed, S^T = K~ Q~^T: a lane owns query columns and a few keys of
+//    each block, so the softmax row max and row sum are in-lane plus exchanges between lane
+//    groups (v_permlane32_swap, and v_permlane16_swap for the 16-lane groups of 16x16 blocks).
 //  * Tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4 (no registers, no VALU) into
 //    four LDS buffers; the copy of tile j+3 is in flight while tile j is consumed, one barrier per
 //    tile.  16-byte chunks are XOR-swizzled by row so that every LDS read below is free of bank
 //    conflicts without padding (the DMA writes each 1 KB block linearly).
 //  * The PV product needs V with keys along each lane's operand; ds_read_b64_tr_b16 reads the
 //    row-major V tile transposed, so V needs no staging pass and no VALU transpose.  The key
-//    order inside each 16 keys matches the order in which the score accumulator hands P^T over
-//    as the B operand (keys 4h..4h+3 then 8+4h..8+4h+3 for lane half h).
+//    order inside the operand matches the order in which the score accumulator hands P^T over as
+//    the B operand.
 //  * The score product of tile j+1 is issued before the softmax of tile j, so the MFMA pipe has
 //    work while the VALU computes exponentials.  The loop is unrolled by the buffer count so all
 //    LDS addresses are a per-lane base plus an immediate.
@@ -69,6 +74,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(1))) const void gptr_t;
@@ -133,10 +139,14 @@ __device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, 
 // Swizzles: logical 16-byte chunk c of tile row r (256 bytes) sits at physical chunk c ^ swz(r).
 // gfx950 LDS serves 256 bytes per clock from 64 banks: 16 lanes of a 16-byte read or 32 lanes
 // of an 8-byte read at a time.  The K operand read has 16 lanes on 16 consecutive rows at one
-// logical chunk; the transposed V read has 32 lanes on 4 consecutive rows x 4 logical chunks
-// (4db .. 4db+3).  With these swizzles each such group touches 16 different physical chunks.
+// logical chunk (both kernels).  The transposed V read of the running-max kernel has 32 lanes on
+// 4 consecutive rows x 4 logical chunks (4db .. 4db+3); that of the fast kernel has 32 lanes on
+// 8 consecutive rows (from a multiple of 8) x 2 logical chunks (2db, 2db+1), so its swizzle maps
+// the 8 rows to 8 different chunk pairs.  With these swizzles each such group touches 16
+// different physical chunks.
 __device__ __forceinline__ int k_swz(int r) { return r & 15; }
 __device__ __forceinline__ int v_swz(int r) { return (r & 3) << 2; }
+__device__ __forceinline__ int v_swz16(int r) { return ((r & 3) << 2) | ((r >> 1) & 2); }
 
 __device__ __forceinline__ float xhalf_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -144,6 +154,17 @@ __device__ __forceinline__ float xhalf_max(float x) {
 }
 __device__ __forceinline__ float xhalf_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane groups).
+__device__ __forceinline__ float xquad_max(float x) {
+    x = xhalf_max(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xquad_sum(float x) {
+    x = xhalf_sum(x);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -154,28 +175,24 @@ constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
 
+// The running-max kernel: 32x32x16 score and PV blocks, the score offset following the lazy
+// running max of every tile.  It serves cross-attention, partial attention, windows, the fused
+// variant and short launches, and as the guard launch it redoes the items the fast launch flagged
+// (p.item_flags non-null: only items whose 8 flag bytes are not all zero).
 // WIN (staged K only): segment s is local window s of p.win, and query, value and output rows are
 // the window's grid rows (win_origin + win_offset) instead of a contiguous run of buffer rows.
-// SAFE: the score offset follows the lazy running max of every tile (the row max of each tile is
-// formed).  !SAFE (the fast launch): the offset is the first tile's row max and is never moved, so
-// a row's sum only grows and bounds every weight it has used; an item whose row sum reaches
-// OVF_SUM = 2^64 (or is not finite) is flagged, and a SAFE guard launch on the same stream redoes
-// exactly the flagged items.  Unflagged, the accumulator stays below 2^64 |v|.
-template <bool FUSED, bool WIN, bool SAFE>
+template <bool FUSED, bool WIN>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     static_assert(!(FUSED && WIN), "window mode reads staged K");
-    static_assert(SAFE || !FUSED, "the fused variant always tracks the running max");
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
     // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
     for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
-        if constexpr (SAFE) {
-            // Guard launch: only the items the fast launch flagged.
-            if (p.item_flags && *reinterpret_cast<const unsigned long long*>(p.item_flags + 8ll * item) == 0)
-                continue;
-        }
+        // Guard launch: only the items the fast launch flagged.
+        if (p.item_flags && *reinterpret_cast<const unsigned long long*>(p.item_flags + 8ll * item) == 0)
+            continue;
         const int logical = xcd_remap(item, p.total_wg);
         const int qt = logical % p.q_tiles;
         const int rest = logical / p.q_tiles;
@@ -423,7 +440,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             constexpr int b1 = (b + 1) % NBUF;
             constexpr int bp = (b + PREF) % NBUF;
             if (ragged && j == ntiles - 1) mask_tail(j, sc);
-            if (SAFE || j == 0) {
+            {
                 const float mx = row_max(sc);   // relative to m_run
                 // Lazy running max: move the offset only when this tile's max is well above it (and on
                 // the first tile, whose scores carry no offset yet).
@@ -534,12 +551,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         // workgroup's LDS is released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-        if constexpr (!SAFE) {
-            // The fast launch never rescales, so the row sum bounds every weight it has used.
-            const bool flagged = __any(!(l_run < OVF_SUM));
-            if (lane == 0) p.item_flags[8ll * item + wave] = flagged ? 1 : 0;
-        }
-
         // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
         const float l_tot = xhalf_sum(l_run);
         const float inv = 1.0f / l_tot;
@@ -557,6 +568,400 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                     u.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
                     *reinterpret_cast<uint2*>(op + d0) = u;
                 }
+        }
+    }  // item
+}
+
+// The fast launch (staged K): 16x16x32 score and PV blocks, and a score offset that is the first
+// tile's row max and never moves.  A row's sum then only grows and bounds every weight it has
+// used; an item whose row sum reaches OVF_SUM = 2^64 (or is not finite) is flagged in
+// p.item_flags, and the guard launch of the running-max kernel on the same stream redoes exactly
+// the flagged items.  Unflagged, the accumulator stays below 2^64 |v|.
+//
+// Against the 32x32x16 blocks of the running-max kernel, the 16x16x32 shape does the same work
+// for about 13 % less energy per product on random operands, and the kernel runs power-limited.
+// Its read addresses take more registers (8 V and 4 K bases), which the running-max kernel's
+// rescaling code has no room for.
+template <bool WIN>
+__global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
+
+    // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
+    // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
+    for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
+        const int logical = xcd_remap(item, p.total_wg);
+        const int qt = logical % p.q_tiles;
+        const int rest = logical / p.q_tiles;
+        const int seg = rest % p.n_segs;
+        const int head = rest / p.n_segs;
+        const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
+        const int win0 = WIN ? win_origin(seg, p.win) : 0;   // window mode: grid row of local row 0
+        const int seg_len = p.seg_len;
+        const int q_len = p.q_len;
+        const long long row_stride = (long long)p.heads * D;
+        const int ntiles = p.k_tiles;
+
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int l16 = lane & 15;
+        const int lg = lane >> 4;
+        const RopeGeom& g = p.g;
+
+        // ---- tile copies ------------------------------------------------------------------------
+        // Wave w, copy i in {0,1}: rows r = 8w + 4i + lane/16, physical chunk lane%16 of that row.
+        const int dr0 = 8 * wave + (lane >> 4);
+        const int pc = lane & 15;
+        const uint16_t* vhead = p.v + (long long)head * D;
+        const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
+        uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
+        int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
+        uint32_t vch2[2];        // the same in bytes
+        const uint32_t rs2 = 2u * (uint32_t)row_stride;   // bytes per V row (< 2^24)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = dr0 + 4 * i;
+            k_src_off[i] = 2u * (uint32_t)(r * D + 8 * (pc ^ k_swz(r)));
+            v_chunk[i] = 8 * (pc ^ v_swz16(r));
+            vch2[i] = 2u * (uint32_t)v_chunk[i];
+        }
+
+        // issue_tile(j, slot): fetch tile j into K and V slot `slot`.
+        auto issue_tile = [&](int j, int slot) {
+            // The wave's LDS base passes through an empty asm so that the copies' LDS addresses are
+            // formed here by scalar adds; hoisted out of the loop, their 16 values were spilled and
+            // reloaded with VALU lane reads on every tile.
+            uint32_t wl = lds0 + (8 * wave) * 256;
+            asm volatile("" : "+s"(wl));
+            const uint32_t kl = wl + slot * TILE_BYTES;
+            const uint32_t vl = wl + V_LDS_BASE + slot * TILE_BYTES;
+            const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
+            if constexpr (WIN) {
+                // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = dr0 + 4 * i;
+                    const int re = r < last ? r : last;
+                    const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
+                    dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+                }
+            } else {
+                const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int r = dr0 + 4 * i;
+                    const int re = r < last ? r : last;
+                    dma16(vt, __umul24((uint32_t)re, rs2) + vch2[i], vl + i * 1024);
+                }
+            }
+            const uint16_t* kt = p.k + (ktile0 + j) * (BN * D);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) dma16(kt, k_src_off[i], kl + i * 1024);
+        };
+        // ---- prologue -----------------------------------------------------------------------------
+#pragma unroll
+        for (int j = 0; j < PREF; ++j) issue_tile(min(j, ntiles - 1), j);
+
+        // ---- queries ------------------------------------------------------------------------------
+        // Lane (l16, lg) owns query columns l16 and 16 + l16 of the wave's 32 rows (qb = 0, 1) and,
+        // as the B operand of the 16x16x32 score product, channels 32 ks + 8 lg .. +7 of each.
+        int q_row[2];
+        bool q_valid[2];
+        f16x8_t qreg[2][4];
+        {
+            // Lanes past the sequence read its first row (in bounds) and are never stored.  Pair p of
+            // a row reads table entry base_a + p, a the axis p falls in: the three bases are formed
+            // once per row, and each pair costs two compares and two selects.  Text rows take
+            // position (0, 0, 0), where every angle is 0 (cos 1, sin 0 exactly): no rotation.
+            const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
+            const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
+            const int lane_p = 4 * lg;   // the pairs of chunk 4 ks + lg are 16 ks + 4 lg + i
+            const int g1 = f1 - lane_p, g2 = f2 - lane_p;
+            const float sc = p.scale_log2;
+            uint4 raw[2][4];
+            int bt[2], bh[2], bw[2];
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const int q_local = qt * BM + wave * 32 + 16 * qb + l16;
+                q_valid[qb] = q_local < q_len;
+                q_row[qb] = WIN ? win0 + win_offset(q_valid[qb] ? q_local : 0, p.win)
+                                : seg * q_len + (q_valid[qb] ? q_local : 0);   // query buffer row
+                const int q_pos = p.q_pos_base + q_row[qb];                   // its global row
+                const bool text = q_pos >= g.Nv;
+                int t, h, w;
+                decode_pos(text ? 0 : q_pos, g, t, h, w);
+                bt[qb] = (int)__umul24((unsigned)t, (unsigned)g.pairs[0]) + lane_p;
+                bh[qb] = g.off[1] - f1 + (int)__umul24((unsigned)h, (unsigned)g.pairs[1]) + lane_p;
+                bw[qb] = g.off[2] - f2 + (int)__umul24((unsigned)w, (unsigned)g.pairs[2]) + lane_p;
+                const uint16_t* qp = p.q + q_row[qb] * row_stride + (long long)head * D + 8 * lg;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) raw[qb][ks] = ld16(qp + 32 * ks);
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    const uint32_t wd[4] = {raw[qb][ks].x, raw[qb][ks].y, raw[qb][ks].z, raw[qb][ks].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int p0 = 16 * ks + i;
+                        const int base = p0 >= g2 ? bw[qb] : (p0 >= g1 ? bh[qb] : bt[qb]);
+                        const float2 cs = p.table[base + p0];
+                        float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
+                        rotate_pair(x0, x1, cs);
+                        o[i] = pack_f16x2(x0 * sc, x1 * sc);
+                    }
+                    qreg[qb][ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+                }
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+
+        // ---- per-lane LDS read addresses (slot 0; other slots add a multiple of TILE_BYTES) --------
+        // K operand of the score product, key block kb (keys 16 kb + l16), step ks: logical chunk
+        // 4 ks + lg of row 16 kb + l16 (the swizzle depends on l16 only).
+        uint32_t k_rd[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) k_rd[ks] = lds0 + l16 * 256 + 16 * ((4 * ks + lg) ^ k_swz(l16));
+        // V operand of the PV product for channel block db, read transposed: the 16 lanes of group
+        // lg read rows 4 lg .. 4 lg + 3 (+ 16 for the upper half, + 32 for the second key chunk) by
+        // channels 16 db .. 16 db + 15.  Lane l16 addresses row 4 lg + l16 / 4 and channels
+        // 16 db + 4 (l16 % 4) .. +3, i.e. logical chunk 2 db + (l16 % 4) / 2, byte 8 (l16 % 2); it
+        // receives channel 16 db + l16 of the four rows.
+        uint32_t v_rd[8];
+        {
+            const int row = 4 * lg + (l16 >> 2);
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
+                v_rd[db] = lds0 + V_LDS_BASE + row * 256 + 16 * ((2 * db + ((l16 & 3) >> 1)) ^ v_swz16(row)) +
+                           8 * (l16 & 1);
+        }
+        auto k_operand = [&](uint32_t kb_slot, int kb, int ks) -> f16x8_t {
+            const uint32_t a = k_rd[ks] + kb_slot + kb * 16 * 256;
+            return *(__attribute__((address_space(3))) const f16x8_t*)(uintptr_t)a;
+        };
+        // Keys of V operand (db, kk): 32 kk + 4 lg + (0..3), then 32 kk + 16 + 4 lg + (0..3).
+        auto v_operand = [&](uint32_t vb, int db, int kk) -> bf16x8_t {
+            const uint32_t a = v_rd[db] + vb + kk * 32 * 256;
+            i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)a);
+            i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t*)(uintptr_t)(a + 16 * 256));
+            return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        // Score block (kb, qb) holds, in lane (l16, lg), keys 16 kb + 4 lg + i (i = 0..3) of query
+        // 16 qb + l16.  Keys of tile j past the end of the sequence get -inf (only the last tile can
+        // have any).  The limit passes through an empty asm so that its compares stay in this
+        // rarely taken branch: hoisted out of the loop they would hold SGPRs for the whole loop.
+        auto mask_tail = [&](int j, f32x4_t (&s)[4][2]) {
+            int lim = seg_len - j * BN - 4 * lg;   // first key offset in the tile past the end
+            asm volatile("" : "+v"(lim));
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * kb + i >= lim) s[kb][qb][i] = -INFINITY;
+        };
+        // Row max of query block qb over a 64-key score tile (all four lane groups).
+        auto row_max = [&](const f32x4_t (&s)[4][2], int qb) -> float {
+            float mx = fmaxf(fmaxf(s[0][qb][0], s[0][qb][1]), s[0][qb][2]);
+            mx = fmaxf(fmaxf(mx, s[0][qb][3]), s[1][qb][0]);
+            mx = fmaxf(fmaxf(mx, s[1][qb][1]), s[1][qb][2]);
+            mx = fmaxf(fmaxf(mx, s[1][qb][3]), s[2][qb][0]);
+            mx = fmaxf(fmaxf(mx, s[2][qb][1]), s[2][qb][2]);
+            mx = fmaxf(fmaxf(mx, s[2][qb][3]), s[3][qb][0]);
+            mx = fmaxf(fmaxf(mx, s[3][qb][1]), s[3][qb][2]);
+            mx = fmaxf(mx, s[3][qb][3]);
+            return xquad_max(mx);
+        };
+
+        // Output O^T block (db, qb): lane (l16, lg) holds channels 16 db + 4 lg + i of query
+        // 16 qb + l16.
+        f32x4_t oacc[8][2];
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) oacc[db][qb][i] = 0.0f;
+        // Scores are in log2 units (q carries log2(e)/sqrt(D)).  m_run is the offset already taken
+        // off every score: the score MFMAs start from negm = -m_run instead of zero.
+        float m_run[2] = {0.0f, 0.0f};
+        float l_run[2] = {0.0f, 0.0f};
+        f32x4_t negm[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) negm[qb][i] = 0.0f;
+        const bool ragged = (seg_len % BN) != 0;
+        const uint32_t one2 = 0x3f803f80u;  // bf16 pair (1, 1)
+
+        // Scores of tile 0.
+        f32x4_t sa[4][2], sb[4][2];
+        {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sa[kb][qb][i] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const f16x8_t ka = k_operand(0, kb, ks);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        sa[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][ks], sa[kb][qb], 0, 0, 0);
+                }
+        }
+
+        // One tile step j (tile j in slot b): softmax weights and PV of tile j (scores sc) while the
+        // scores of tile j+1 (sn) are formed and tile j+PREF is fetched into slot (b+PREF) % NBUF.
+        auto step = [&](auto bufc, int j, f32x4_t (&sc)[4][2], f32x4_t (&sn)[4][2]) {
+            constexpr int b = decltype(bufc)::value;
+            constexpr int b1 = (b + 1) % NBUF;
+            constexpr int bp = (b + PREF) % NBUF;
+            if (ragged && j == ntiles - 1) mask_tail(j, sc);
+            if (j == 0) {
+                // The offset: the first tile's row max, taken off its scores and, through negm, off
+                // every later score.
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    const float mx = row_max(sc, qb);
+                    m_run[qb] = mx;
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sc[kb][qb][i] -= mx;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) negm[qb][i] = -mx;
+                }
+            }
+
+            // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
+            // last tile the K slot holds stale data and these scores are discarded.
+            // B operand of PV chunk kk (keys 32 kk ..) for query block qb: blocks 2 kk and 2 kk + 1.
+            // The rounded weights are summed in two chains, one of them the running row sum.
+            bf16x8_t pb[2][2];
+            float l2[2] = {0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    uint32_t u[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int kb = 2 * kk + (e >> 1), i0 = 2 * (e & 1);
+                        const float p0 = __builtin_amdgcn_exp2f(sc[kb][qb][i0]);
+                        const float p1 = __builtin_amdgcn_exp2f(sc[kb][qb][i0 + 1]);
+                        u[e] = pack_bf16x2(p0, p1);
+                        if (kk)
+                            l2[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                                     __builtin_bit_cast(bf16x2_t, one2), l2[qb], false);
+                        else
+                            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                                                                        __builtin_bit_cast(bf16x2_t, one2), l_run[qb], false);
+                    }
+                    pb[kk][qb] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
+                }
+            l_run[0] += l2[0];
+            l_run[1] += l2[1];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const f16x8_t ka = k_operand(b1 * TILE_BYTES, kb, ks);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        sn[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][ks],
+                                                                            ks == 0 ? negm[qb] : sn[kb][qb], 0, 0, 0);
+                }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+            }
+
+            // Fetch tile j+PREF into the slot read last before the previous barrier.  Past the last
+            // tile the fetch repeats the last tile into that free slot (nothing reads it again);
+            // issuing unconditionally keeps the count of copies in flight fixed.
+            issue_tile(min(j + PREF, ntiles - 1), bp);
+
+            // PV of tile j.
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    const bf16x8_t va = v_operand(b * TILE_BYTES, db, kk);
+#pragma unroll
+                    for (int qb = 0; qb < 2; ++qb)
+                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk][qb], oacc[db][qb], 0, 0, 0);
+                }
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+#pragma unroll
+            for (int t = 0; t < 13; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 6, 0);
+
+            // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
+            asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+        };
+
+        for (int j = 0; j < ntiles; j += 4) {
+            step(Buf<0>{}, j, sa, sb);
+            if (j + 1 >= ntiles) break;
+            step(Buf<1>{}, j + 1, sb, sa);
+            if (j + 2 >= ntiles) break;
+            step(Buf<2>{}, j + 2, sa, sb);
+            if (j + 3 >= ntiles) break;
+            step(Buf<3>{}, j + 3, sb, sa);
+        }
+        // Copies issued by the last steps (repeats of the last tile) must land before the
+        // workgroup's LDS is released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+        {
+            // Never rescaled, a lane's partial row sums bound every weight it has used.
+            const bool flagged = __any(!(l_run[0] < OVF_SUM) || !(l_run[1] < OVF_SUM));
+            if (lane == 0) p.item_flags[8ll * item + wave] = flagged ? 1 : 0;
+        }
+
+        // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float l_tot = xquad_sum(l_run[qb]);
+            const float inv = 1.0f / l_tot;
+            if (p.lse && q_valid[qb] && lg == 0)
+                p.lse[(long long)q_row[qb] * p.heads + head] = m_run[qb] * 0.6931471805599453f + __logf(l_tot);
+            if (q_valid[qb]) {
+                uint16_t* op = p.out + q_row[qb] * row_stride + (long long)head * D + 4 * lg;
+#pragma unroll
+                for (int db = 0; db < 8; ++db) {
+                    uint2 u;
+                    u.x = pack_bf16x2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv);
+                    u.y = pack_bf16x2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
+                    *reinterpret_cast<uint2*>(op + 16 * db) = u;
+                }
+            }
         }
     }  // item
 }
@@ -644,15 +1049,15 @@ hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
     if constexpr (!FUSED) {
         if (flags && (long long)p.total_wg * p.k_tiles >= kFastMinTiles) {
             p.item_flags = flags;
-            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN, false>), grid, dim3(NTHREADS), 0, stream, p);
+            hipLaunchKernelGGL((attn_fast_kernel<WIN>), grid, dim3(NTHREADS), 0, stream, p);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN, true>), grid, dim3(NTHREADS), 0, stream, p);
+            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN>), grid, dim3(NTHREADS), 0, stream, p);
             return hipGetLastError();
         }
     }
     p.item_flags = nullptr;
-    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, WIN, true>), grid, dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<FUSED, WIN>), grid, dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

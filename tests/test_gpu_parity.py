@@ -167,17 +167,19 @@ def test_running_max_keeps_growing(dtype):
         assert rel <= 5e-3 and max_abs <= 5e-2
 
 
-# The attend step runs a fast kernel (score offset from each row's first 64 keys, never moved)
-# and a guard launch that redoes, with the running-max kernel, every 256-row block whose weights
-# reached 2^20.  It does so from 32768 (block, 64-key tile) pairs up; 16384 tokens x 2 heads is
-# the smallest grid of that size.  The partial-attention entry point runs the running-max kernel
-# alone over the same rows.
+# The attend step runs a fast kernel (16x16x32 blocks; score offset from each row's first 64 keys,
+# never moved) and a guard launch that redoes, with the running-max kernel (32x32x16 blocks), every
+# 256-row block whose row sums reached 2^64.  It does so from 32768 (block, 64-key tile) pairs up;
+# 16384 tokens x 2 heads is the smallest grid of that size.  The partial-attention entry point runs
+# the running-max kernel alone over the same rows.
 FAST_GRID = (8, 32, 64)
 
 
-def test_fast_launch_equals_running_max_kernel_bitwise():
-    """N(0,1) inputs never move a row's maximum by more than 8 after the first tile, so the fast
-    launch and the running-max kernel do the same arithmetic."""
+def test_fast_launch_agrees_with_running_max_kernel():
+    """N(0,1) inputs never move a row's maximum by more than 8 after the first tile, so the two
+    kernels evaluate the same weights; they differ only in the order of their fp32 sums (and so
+    in a few roundings of weights and outputs to bf16).  Each meets the parity bar against the
+    oracle on sampled rows, and the two agree to a fifth of the relative-L2 bar everywhere."""
     n = 8 * 32 * 64
     log(f"  fast launch vs running-max kernel grid={FAST_GRID} heads=2 dtype=bf16 seed=330")
     x = make_qkv(n, 2, 128, 330, "bf16")
@@ -185,13 +187,21 @@ def test_fast_launch_equals_running_max_kernel_bitwise():
     fast = fa.attn3d(q, k, v, FAST_GRID)
     safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
     torch.cuda.synchronize()
-    assert torch.equal(fast.view(torch.int16), safe.view(torch.int16))
+    got_fast, got_safe = host_f64(fast), host_f64(safe)
+    max_abs, rel = errors(got_fast, got_safe)
+    same = float(np.mean(got_fast == got_safe))
+    log(f"    fast vs running-max: max_abs={max_abs:.3e} rel_l2={rel:.3e} identical={same:.3f}")
+    assert rel <= 1e-3 and max_abs <= 2e-3
+    rows = sample_rows(n, n, 2048, 256, 330)
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, FAST_GRID, 0, WAN, 10000.0, rows=rows, heads=[0, 1])
+    assert_close(got_fast[rows], ref, "bf16", "fast launch")
+    assert_close(got_safe[rows], ref, "bf16", "running-max kernel")
 
 
 @pytest.mark.parametrize("q_mult,k_ramp", [(2.0, 1.5), (6.0, 3.0)])
 def test_fast_launch_redoes_blocks_whose_weights_grow(q_mult, k_ramp):
     """Keys whose norm grows along the sequence: later tiles score far above the first one, the
-    fast launch flags those blocks (weights past 2^20, or infinite) and the guard redoes them."""
+    fast launch flags those blocks (row sums past 2^64, or infinite) and the guard redoes them."""
     n = 8 * 32 * 64
     rows = sample_rows(n, n, 2048, 384, 331)
     got, ref = run_full(FAST_GRID, 2, "bf16", 331, rows=rows, q_mult=q_mult, k_ramp=k_ramp)
