@@ -882,9 +882,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                         sn[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][ks],
                                                                             ks == 0 ? negm[qb] : sn[kb][qb], 0, 0, 0);
                 }
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < 12; ++t) {
                 __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
@@ -892,7 +892,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                 __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
             }
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
+            for (int t = 0; t < 8; ++t) {
                 __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
             }
@@ -912,13 +912,13 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                     for (int qb = 0; qb < 2; ++qb)
                         oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk][qb], oacc[db][qb], 0, 0, 0);
                 }
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
 #pragma unroll
-            for (int t = 0; t < 13; ++t) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+            for (int t = 0; t < 28; ++t) {
+                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
 
             // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
