@@ -538,14 +538,30 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             asm volatile("" ::: "memory");
         };
 
-        for (int j = 0; j < ntiles; j += 4) {
-            step(Buf<0>{}, j, sa, sb);
-            if (j + 1 >= ntiles) break;
-            step(Buf<1>{}, j + 1, sb, sa);
-            if (j + 2 >= ntiles) break;
-            step(Buf<2>{}, j + 2, sa, sb);
-            if (j + 3 >= ntiles) break;
-            step(Buf<3>{}, j + 3, sb, sa);
+        if (qt * BM + wave * 32 < q_len) {
+            for (int j = 0; j < ntiles; j += 4) {
+                step(Buf<0>{}, j, sa, sb);
+                if (j + 1 >= ntiles) break;
+                step(Buf<1>{}, j + 1, sb, sa);
+                if (j + 2 >= ntiles) break;
+                step(Buf<2>{}, j + 2, sa, sb);
+                if (j + 3 >= ntiles) break;
+                step(Buf<3>{}, j + 3, sb, sa);
+            }
+        } else {
+            // All 32 query rows of this wave lie past the sequence (the last query tile of a short
+            // sequence): no products, only this wave's share of the tile copies and the barriers.
+            for (int j = 0; j < ntiles; ++j) {
+                issue_tile(min(j + PREF, ntiles - 1), (j + PREF) % NBUF);
+                if constexpr (FUSED) {
+                    finish_tile(min(j + PREF, ntiles - 1), (j + PREF) % NBUF);
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                }
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
         }
         // Copies issued by the last steps (repeats of the last tile) must land before the
         // workgroup's LDS is released.
@@ -926,14 +942,25 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
             asm volatile("" ::: "memory");
         };
 
-        for (int j = 0; j < ntiles; j += 4) {
-            step(Buf<0>{}, j, sa, sb);
-            if (j + 1 >= ntiles) break;
-            step(Buf<1>{}, j + 1, sb, sa);
-            if (j + 2 >= ntiles) break;
-            step(Buf<2>{}, j + 2, sa, sb);
-            if (j + 3 >= ntiles) break;
-            step(Buf<3>{}, j + 3, sb, sa);
+        if (qt * BM + wave * 32 < q_len) {
+            for (int j = 0; j < ntiles; j += 4) {
+                step(Buf<0>{}, j, sa, sb);
+                if (j + 1 >= ntiles) break;
+                step(Buf<1>{}, j + 1, sb, sa);
+                if (j + 2 >= ntiles) break;
+                step(Buf<2>{}, j + 2, sa, sb);
+                if (j + 3 >= ntiles) break;
+                step(Buf<3>{}, j + 3, sb, sa);
+            }
+        } else {
+            // All 32 query rows of this wave lie past the sequence (the last query tile of a short
+            // sequence): no products, only this wave's share of the tile copies and the barriers.
+            for (int j = 0; j < ntiles; ++j) {
+                issue_tile(min(j + PREF, ntiles - 1), (j + PREF) % NBUF);
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+            }
         }
         // Copies issued by the last steps (repeats of the last tile) must land before the
         // workgroup's LDS is released.
