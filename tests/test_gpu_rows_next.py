@@ -262,3 +262,31 @@ def test_window_wan_grid_sampled():
     rows = sample_rows(n, n, 1560, 512, 7633)
     ref = oracle.window_attention_ref(x.q, x.k, x.v, grid, window, WAN, rows=rows)
     assert_close(host_f64(out)[rows], ref, "bf16", "window 21x30x52 / 7x10x13 sampled")
+
+
+# Windows large enough that the attend step takes the fast launch (at least 32768 pairs of a
+# 256-row block and a 64-key tile), so the 16x16x32 kernel's window row map runs as well.
+def test_window_fast_launch_ragged_sampled():
+    """4 windows of 7x15x26 = 2730 tokens (a partial last key tile, and a last query block whose
+    last two waves have no rows), 20 heads: 4 x 11 blocks x 20 heads x 43 key tiles = 37840."""
+    grid, window, heads = (7, 30, 52), (7, 15, 26), 20
+    n = 7 * 30 * 52
+    log(f"  window grid={grid} window={window} heads={heads} dtype=bf16 seed=7640 rows=384")
+    x, (q, k, v) = grid_inputs(grid, 0, heads, "bf16", 7640, WAN)
+    out = fa.attn_window(q, k, v, grid, window)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, n, 1560, 384, 7641)
+    ref = oracle.window_attention_ref(x.q, x.k, x.v, grid, window, WAN, rows=rows)
+    assert_close(host_f64(out)[rows], ref, "bf16", "window 7x30x52 / 7x15x26, fast launch, sampled")
+
+
+def test_window_over_whole_grid_fast_launch_bitwise():
+    """One window over a 16,384-token grid, 2 heads (64 blocks x 2 heads x 256 key tiles = 32768):
+    both calls take the fast launch, and with the identity row map they agree bit for bit."""
+    grid = (8, 32, 64)
+    log(f"  window grid={grid} window=grid vs attn3d (fast launch) dtype=bf16 seed=7650")
+    _, (q, k, v) = grid_inputs(grid, 0, 2, "bf16", 7650, WAN)
+    a = fa.attn_window(q, k, v, grid, grid)
+    b = fa.attn3d(q, k, v, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
