@@ -91,7 +91,7 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  *   attend: the attention kernel; it rotates Q itself and streams the staged K tiles and the
  *           caller's V.  It runs in two launches: the first takes each row's score offset from
  *           its first 64 keys only and flags in the workspace any block of 256 query rows whose
- *           softmax row sums (taken against that offset) reach 2^64 or are not finite; the second
+ *           softmax row sums (taken against that offset) reach 2^64, infinity included; the second
  *           redoes only flagged blocks with a running maximum over every 64 keys.  Attention over
  *           fewer than 32768 (block, 64-key tile) pairs runs the second kind alone.
  * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
