@@ -13,6 +13,8 @@
 // of 32 x 32.  K advances 64 at a time through two LDS stages (x tile and W tile, 32 KB each),
 // copied by LDS DMA one stage ahead of the MFMAs.  The output tile goes through LDS so that rows
 // are written whole.
+#include <type_traits>
+
 #include "st_internal.h"
 
 namespace st {
@@ -176,68 +178,101 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
     // 64 fg + 32 fb + 8 (i / 4) + 4 hh + i % 4 of the tile.
     const RopeGeom& g = p.g;
     // The lane's 32 features are the same for all four token blocks: their bias is loaded once.
-    // Table entries of token block tb + 1 are loaded while block tb is rotated and stored.
-    const bool has_bias = p.bias != nullptr;
+    // Tiles that end inside the last output feature (heads odd) test each load.
     uint2 bw[2][4];
+    const bool bias_full = p.bias != nullptr && f0 + GN <= F;
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
             const int f = f0 + 64 * fg + 32 * fb + 8 * gi + 4 * hh;
-            bw[fb][gi] = (has_bias && f < F) ? *reinterpret_cast<const uint2*>(p.bias + f) : make_uint2(0u, 0u);
+            bw[fb][gi] = make_uint2(0u, 0u);
+            if (bias_full)
+                bw[fb][gi] = *reinterpret_cast<const uint2*>(p.bias + f);
+            else if (p.bias != nullptr && f < F)
+                bw[fb][gi] = *reinterpret_cast<const uint2*>(p.bias + f);
         }
-    // Pair entries of token block tb for the q and k features of this lane (v features: unused).
-    auto load_cs = [&](int tb, float2 (&cs)[2][4][2]) {
-        const int row = 128 * tg + 32 * tb + l32;
-        const int n = min(m0 + row, p.n_rows - 1);
-        int t = 0, h = 0, w = 0;
-        const bool text = n >= g.Nv;
-        if (!text) decode_pos(n, g, t, h, w);
+    // A tile's 256 features are all q and k features (rotated) or all v features: 2C = heads x 256
+    // is a multiple of the tile width, so the choice is one branch per workgroup.
+    const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
+    const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
+    const int o0 = __builtin_amdgcn_readfirstlane(g.off[0]);
+    const int o1 = __builtin_amdgcn_readfirstlane(g.off[1]);
+    const int o2 = __builtin_amdgcn_readfirstlane(g.off[2]);
+    const int s0 = __builtin_amdgcn_readfirstlane(g.pairs[0]);
+    const int s1 = __builtin_amdgcn_readfirstlane(g.pairs[1]);
+    const int s2 = __builtin_amdgcn_readfirstlane(g.pairs[2]);
+    const int lane_p = 32 * (fg & 1) + 2 * hh;
+    const int g1 = f1 - lane_p, g2 = f2 - lane_p;
+    auto finish = [&](auto rotc) {
+        constexpr bool ROT = decltype(rotc)::value;
+        // Pair entries of token block tb for this lane's features.  The lane's pairs are
+        // lane_p + 16 fb + 4 gi + e of the head (lane_p = 32 (fg % 2) + 2 hh), the same for every
+        // token: per token the three axis bases are formed once, and each pair costs two compares,
+        // two selects and an add.  Text rows take position (0, 0, 0), where every angle is 0.
+        auto load_cs = [&](int tb, float2 (&cs)[2][4][2]) {
+            if constexpr (ROT) {
+                const int row = 128 * tg + 32 * tb + l32;
+                const int n = min(m0 + row, p.n_rows - 1);
+                const bool text = n >= g.Nv;
+                int t, h, w;
+                decode_pos(text ? 0 : n, g, t, h, w);
+                const int bt = o0 + (int)__umul24((unsigned)t, (unsigned)s0) + lane_p;
+                const int bh = o1 - f1 + (int)__umul24((unsigned)h, (unsigned)s1) + lane_p;
+                const int bw = o2 - f2 + (int)__umul24((unsigned)w, (unsigned)s2) + lane_p;
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
+                for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const int f = f0 + 64 * fg + 32 * fb + 8 * gi + 4 * hh;
-                const int pair = (f % 128) >> 1;
+                    for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    cs[fb][gi][e] = f < 2 * C ? p.table[pair_entry(pair + e, t, h, w, text, g)]
-                                              : make_float2(1.0f, 0.0f);
+                        for (int e = 0; e < 2; ++e) {
+                            const int k = 16 * fb + 4 * gi + e;
+                            const int base = k >= g2 ? bw : (k >= g1 ? bh : bt);
+                            cs[fb][gi][e] = p.table[base + k];
+                        }
+            } else {
+                (void)tb;
+                (void)cs;
             }
-    };
-    float2 csa[2][4][2], csb[2][4][2];
-    auto block = [&](int tb, const float2 (&cs)[2][4][2]) {
-        const int row = 128 * tg + 32 * tb + l32;     // token row inside the tile
+        };
+        auto block = [&](int tb, const float2 (&cs)[2][4][2]) {
+            const int row = 128 * tg + 32 * tb + l32;     // token row inside the tile
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb)
+            for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const int fl = 64 * fg + 32 * fb + 8 * gi + 4 * hh;   // first of 4 features, in tile
-                const int f = f0 + fl;
-                float y[4];
+                for (int gi = 0; gi < 4; ++gi) {
+                    const int fl = 64 * fg + 32 * fb + 8 * gi + 4 * hh;   // first of 4 features, in tile
+                    float y[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][4 * gi + e];
-                y[0] += bf16_lo(bw[fb][gi].x);
-                y[1] += bf16_hi(bw[fb][gi].x);
-                y[2] += bf16_lo(bw[fb][gi].y);
-                y[3] += bf16_hi(bw[fb][gi].y);
-                if (f < 2 * C) {                  // q or k: rotate pairs (f, f+1), (f+2, f+3)
+                    for (int e = 0; e < 4; ++e) y[e] = acc[fb][tb][4 * gi + e];
+                    y[0] += bf16_lo(bw[fb][gi].x);
+                    y[1] += bf16_hi(bw[fb][gi].x);
+                    y[2] += bf16_lo(bw[fb][gi].y);
+                    y[3] += bf16_hi(bw[fb][gi].y);
+                    if constexpr (ROT) {   // q or k: rotate pairs (f, f+1), (f+2, f+3)
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) rotate_pair(y[2 * e], y[2 * e + 1], cs[fb][gi][e]);
+                        for (int e = 0; e < 2; ++e) rotate_pair(y[2 * e], y[2 * e + 1], cs[fb][gi][e]);
+                    }
+                    const u32x2_t pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+                    const uint32_t a = lds0 + row * 512 + 16 * ((fl >> 3) ^ (row & 31)) + 8 * hh;
+                    *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)a = pk;
                 }
-                const u32x2_t pk = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-                const uint32_t a = lds0 + row * 512 + 16 * ((fl >> 3) ^ (row & 31)) + 8 * hh;
-                *(__attribute__((address_space(3))) u32x2_t*)(uintptr_t)a = pk;
-            }
+        };
+        // Table entries of token block tb + 1 are loaded while block tb is rotated and stored.
+        float2 csa[2][4][2], csb[2][4][2];
+        load_cs(0, csa);
+        load_cs(1, csb);
+        block(0, csa);
+        load_cs(2, csa);
+        block(1, csb);
+        load_cs(3, csb);
+        block(2, csa);
+        block(3, csb);
     };
-    load_cs(0, csa);
-    load_cs(1, csb);
-    block(0, csa);
-    load_cs(2, csa);
-    block(1, csb);
-    load_cs(3, csb);
-    block(2, csa);
-    block(3, csb);
+    if (f0 < 2 * C)
+        finish(std::true_type{});
+    else
+        finish(std::false_type{});
     __syncthreads();
     // Wave w writes tile rows 32 w .. +31, two rows (2 x 512 bytes) per store.
 #pragma unroll 4
