@@ -122,13 +122,13 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 // Rotate 8 bf16 channels (pairs 4c .. 4c+3) of a row at (t, h, w) and return them as fp16.
-__device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, int w, bool text,
+__device__ __forceinline__ uint4 rope_chunk_f16(uint4 raw, int c, int t, int h, int w,
                                                 const RopeGeom& g, const float2* __restrict__ table,
                                                 float scale = 1.0f) {
     uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float2 cs = table[pair_entry(4 * c + i, t, h, w, text, g)];
+        float2 cs = table[pair_entry(4 * c + i, t, h, w, g)];
         float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
         rotate_pair(x0, x1, cs);
         wd[i] = pack_f16x2(x0 * scale, x1 * scale);
@@ -283,7 +283,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
                     int t = 0, h = 0, w = 0;
                     const bool text = n >= g.Nv;
                     if (!text) decode_pos(n, g, t, h, w);
-                    uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, text, g, p.table);
+                    uint4 rot = rope_chunk_f16(i == 0 ? fk0 : fk1, fkc, t, h, w, g, p.table);
                     const uint32_t a = lds0 + slot * TILE_BYTES + r * 256 + 16 * (fkc ^ k_swz(r));
                     const u32x4_t rv = {rot.x, rot.y, rot.z, rot.w};
                     *(__attribute__((address_space(3))) u32x4_t*)(uintptr_t)a = rv;
@@ -1018,7 +1018,7 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
         int t = 0, h = 0, w = 0;
         const bool text = n >= g.Nv;
         if (!text) decode_pos(n, g, t, h, w);
-        *reinterpret_cast<uint4*>(out + r * D + 8 * c) = rope_chunk_f16(raw, c, t, h, w, text, g, p.table);
+        *reinterpret_cast<uint4*>(out + r * D + 8 * c) = rope_chunk_f16(raw, c, t, h, w, g, p.table);
     }
 }
 

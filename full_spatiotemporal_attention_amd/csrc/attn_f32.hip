@@ -65,7 +65,7 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
         const float* qp = p.q + qrow * rs + (long long)head * d;
         for (int pp = 0; pp < half; ++pp) {
             float2 x = qv ? *reinterpret_cast<const float2*>(qp + 2 * pp) : make_float2(0.f, 0.f);
-            rotate_pair(x.x, x.y, p.table[pair_entry(pp, t, h, w, text, g)]);
+            rotate_pair(x.x, x.y, p.table[pair_entry(pp, t, h, w, g)]);
             lds_q[(2 * pp) * QB + tid] = x.x;
             lds_q[(2 * pp + 1) * QB + tid] = x.y;
         }
@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(QB) attn_f32_kernel(F32Params p) {
             row_pos(L.kv_pos_base + krow, g, t, h, w, text);
             const long long base = krow * rs + (long long)head * d + 2 * pp;
             float2 x = *reinterpret_cast<const float2*>(p.k + base);
-            rotate_pair(x.x, x.y, p.table[pair_entry(pp, t, h, w, text, g)]);
+            rotate_pair(x.x, x.y, p.table[pair_entry(pp, t, h, w, g)]);
             lds_k[r * DMAX + 2 * pp] = x.x;
             lds_k[r * DMAX + 2 * pp + 1] = x.y;
             float2 vv = *reinterpret_cast<const float2*>(p.v + base);

@@ -44,7 +44,7 @@ __device__ __forceinline__ uint4 rope_chunk(uint4 raw, int c, int t, int h, int 
     uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float2 cs = table[pair_entry(4 * c + i, t, h, w, false, g)];
+        float2 cs = table[pair_entry(4 * c + i, t, h, w, g)];
         float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
         rotate_pair(x0, x1, cs);
         f16x2_t hv = {(_Float16)x0, (_Float16)x1};

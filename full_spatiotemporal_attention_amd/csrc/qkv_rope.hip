@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(256) qkv_rope_f32_kernel(QkvF32Params p) {
             for (int e = 0; e < 2; ++e) {
                 const int f = fb + 2 * e;
                 const int pair = (f % p.d) >> 1;
-                rotate_pair(y[2 * e], y[2 * e + 1], p.table[pair_entry(pair, t, h, w, text, g)]);
+                rotate_pair(y[2 * e], y[2 * e + 1], p.table[pair_entry(pair, t, h, w, g)]);
             }
         }
 #pragma unroll

@@ -58,7 +58,7 @@ __global__ void __launch_bounds__(256) rope_apply_bf16_kernel(const uint16_t* x,
         uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int pi = 0; pi < 4; ++pi) {
-            float2 cs = table[pair_entry(4 * c + pi, t, h, w, text, g)];
+            float2 cs = table[pair_entry(4 * c + pi, t, h, w, g)];
             float x0 = bf16_lo(wds[pi]), x1 = bf16_hi(wds[pi]);
             rotate_pair(x0, x1, cs);
             wds[pi] = pack_bf16x2(x0, x1);
@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(256) rope_apply_f32_kernel(const float* x,
         bool text = n >= g.Nv;
         if (!text) decode_pos(n, g, t, h, w);
         float2 v = *reinterpret_cast<const float2*>(x + i * 2);
-        rotate_pair(v.x, v.y, table[pair_entry(p, t, h, w, text, g)]);
+        rotate_pair(v.x, v.y, table[pair_entry(p, t, h, w, g)]);
         *reinterpret_cast<float2*>(y + i * 2) = v;
     }
 }

@@ -82,11 +82,13 @@ __device__ __forceinline__ int win_offset(int li, const WinMap& m) {
     return li + lt * m.A + lh * m.B;
 }
 
-// Table entry of head pair `p` (0 .. d/2-1) for a row at (t, h, w); text rows get the identity.
+// Table entry of head pair `p` (0 .. d/2-1) for a row at (t, h, w).  Text rows pass position
+// (0, 0, 0), whose entries hold angle 0, i.e. (1, 0) exactly: no rotation, and no branch on the
+// row kind (a select on it became a divergent branch around every table load).
 // The geometry fields are uniform: they are taken into scalar registers once and the axis is
 // chosen between values (a choice between array elements would become a per-lane memory load).
 // pos * stride < 2^24, so the product is a 24-bit multiply.
-__device__ __forceinline__ int pair_entry(int p, int t, int h, int w, bool text, const RopeGeom& g) {
+__device__ __forceinline__ int pair_entry(int p, int t, int h, int w, const RopeGeom& g) {
     const int f1 = __builtin_amdgcn_readfirstlane(g.first[1]);
     const int f2 = __builtin_amdgcn_readfirstlane(g.first[2]);
     const int o0 = __builtin_amdgcn_readfirstlane(g.off[0]);
@@ -95,13 +97,12 @@ __device__ __forceinline__ int pair_entry(int p, int t, int h, int w, bool text,
     const int s0 = __builtin_amdgcn_readfirstlane(g.pairs[0]);
     const int s1 = __builtin_amdgcn_readfirstlane(g.pairs[1]);
     const int s2 = __builtin_amdgcn_readfirstlane(g.pairs[2]);
-    const int ident = __builtin_amdgcn_readfirstlane(g.identity);
     const bool a1 = p >= f1, a2 = p >= f2;
     const int first = a2 ? f2 : (a1 ? f1 : 0);
     const int base = a2 ? o2 : (a1 ? o1 : o0);
     const int stride = a2 ? s2 : (a1 ? s1 : s0);
     const int pos = a2 ? w : (a1 ? h : t);
-    return text ? ident : base + (int)__umul24((unsigned)pos, (unsigned)stride) + (p - first);
+    return base + (int)__umul24((unsigned)pos, (unsigned)stride) + (p - first);
 }
 
 // bfloat16 helpers (storage is uint16_t; conversions are exact widening and RNE narrowing).
