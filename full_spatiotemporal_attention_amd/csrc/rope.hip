@@ -37,33 +37,51 @@ hipError_t launch_rope_table(const RopeGeom& g, double theta, float2* table, hip
     return hipGetLastError();
 }
 
-// bf16: one thread handles 8 channels (4 pairs, 16 bytes) of one (row, head).  HBM bound:
-// every input byte is read once and every output byte written once.  x and y may be the same
-// buffer: each thread reads its 16 bytes before writing them back.
+// bf16 (d = 128): one wave per row.  Lane l takes the 16-byte chunk c = l % 16 (channels 8c ..
+// 8c+7, pairs 4c .. 4c+3) of heads l / 16, l / 16 + 4, ...: the row's position is decoded once
+// per wave, and the lane's four table entries serve every head of the row.  HBM bound: every
+// input byte is read once and every output byte written once.  x and y may be the same buffer:
+// each lane reads its 16 bytes before writing them back.  Text rows take position (0, 0, 0),
+// whose angles are 0: they are copied unchanged.
 __global__ void __launch_bounds__(256) rope_apply_bf16_kernel(const uint16_t* x,
                                                               uint16_t* y, RopeGeom g,
-                                                              int N, int heads, int d,
+                                                              int N, int heads,
                                                               const float2* __restrict__ table) {
-    const int chunks_per_row = d >> 3;
-    const long long total = (long long)N * heads * chunks_per_row;
-    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (long long)gridDim.x * blockDim.x) {
-        long long rh = i / chunks_per_row;
-        int c = (int)(i - rh * chunks_per_row);
-        int n = (int)(rh / heads);
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int h0 = lane >> 4;
+    const int waves = gridDim.x * 4;
+    for (int n = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (int)(threadIdx.x >> 6)); n < N; n += waves) {
         int t = 0, h = 0, w = 0;
-        bool text = n >= g.Nv;
-        if (!text) decode_pos(n, g, t, h, w);
-        uint4 raw = *reinterpret_cast<const uint4*>(x + i * 8);
-        uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+        if (n < g.Nv) decode_pos(n, g, t, h, w);
+        float2 cs[4];
 #pragma unroll
-        for (int pi = 0; pi < 4; ++pi) {
-            float2 cs = table[pair_entry(4 * c + pi, t, h, w, g)];
-            float x0 = bf16_lo(wds[pi]), x1 = bf16_hi(wds[pi]);
-            rotate_pair(x0, x1, cs);
-            wds[pi] = pack_bf16x2(x0, x1);
+        for (int pi = 0; pi < 4; ++pi) cs[pi] = table[pair_entry(4 * c + pi, t, h, w, g)];
+        const long long rb = (long long)n * heads * 128 + 8 * c;   // (row n, head 0, chunk c)
+        // Up to 16 heads per pass; all of a pass's loads are issued before its first store (x and
+        // y may alias, so the compiler would not move a load above an earlier store).
+        for (int hb = 0; hb < heads; hb += 16) {
+            uint4 raw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int hd = hb + h0 + 4 * k;
+                if (hd < heads) raw[k] = *reinterpret_cast<const uint4*>(x + rb + (long long)hd * 128);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int hd = hb + h0 + 4 * k;
+                if (hd < heads) {
+                    uint32_t wds[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+                    for (int pi = 0; pi < 4; ++pi) {
+                        float x0 = bf16_lo(wds[pi]), x1 = bf16_hi(wds[pi]);
+                        rotate_pair(x0, x1, cs[pi]);
+                        wds[pi] = pack_bf16x2(x0, x1);
+                    }
+                    *reinterpret_cast<uint4*>(y + rb + (long long)hd * 128) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                }
+            }
         }
-        *reinterpret_cast<uint4*>(y + i * 8) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
     }
 }
 
@@ -98,9 +116,13 @@ static int stream_grid(long long work, int threads) {
 
 hipError_t launch_rope_apply_bf16(const uint16_t* x, uint16_t* y, const RopeGeom& g, int N,
                                   int heads, int d, const float2* table, hipStream_t stream) {
-    long long work = (long long)N * heads * (d / 8);
-    hipLaunchKernelGGL(rope_apply_bf16_kernel, dim3(stream_grid(work, 256)), dim3(256), 0, stream,
-                       x, y, g, N, heads, d, table);
+    if (d != 128) return hipErrorInvalidValue;
+    // One wave per row, four rows per workgroup, up to 64 rows per wave.
+    long long blocks = ((long long)N + 3) / 4;
+    const long long cap = 256LL * 128;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(rope_apply_bf16_kernel, dim3((int)blocks), dim3(256), 0, stream,
+                       x, y, g, N, heads, table);
     return hipGetLastError();
 }
 

@@ -73,7 +73,9 @@ def test_rope_table(grid, split):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("grid,n_text,heads,split", [((3, 4, 6), 0, 2, WAN), ((5, 7, 11), 9, 3, HUN),
-                                                     ((21, 30, 52), 0, 12, WAN)])
+                                                     ((21, 30, 52), 0, 12, WAN),
+                                                     ((2, 3, 4), 5, 24, HUN),    # heads in two passes of 16
+                                                     ((1, 2, 3), 0, 40, WAN)])   # and three
 def test_rope_apply(dtype, grid, n_text, heads, split):
     T, H, W = grid
     n = T * H * W + n_text
