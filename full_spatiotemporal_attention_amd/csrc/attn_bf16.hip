@@ -993,32 +993,58 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
     }  // item
 }
 
-// Staging for the default mode: one workgroup per (head, segment, key tile) rotates the tile's
-// 64 K rows into fp16.  Rows past the segment are written as zeros.  WIN: segment s is window s.
+// Staging for the default mode: the K rows of every (segment, key tile) rotated into fp16 tiles,
+// [head][segment][tile][64][D].  One wave per tile row: lane l takes the 16-byte chunk l % 16 of
+// heads l / 16, l / 16 + 4, ..., so the row's position is decoded once per wave and the lane's
+// four table entries serve all of its heads; a pass issues the loads of up to 16 heads before its
+// stores.  Rows past the segment are written as zeros.  WIN: segment s is window s.
 template <bool WIN>
 __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
-    const int tile = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15;
+    const int h0 = lane >> 4;
+    const int rt = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (int)(threadIdx.x >> 6));   // tile row
+    const int r = rt & (BN - 1);
+    const int tile = rt / BN;                  // segment * k_tiles + key tile
     const int kt = tile % p.k_tiles;
-    const int rest = tile / p.k_tiles;
-    const int seg = rest % p.n_segs;
-    const int head = rest / p.n_segs;
+    const int seg = tile / p.k_tiles;
     const long long row_stride = (long long)p.heads * D;
     const RopeGeom& g = p.g;
-    uint16_t* out = p.kt + (long long)tile * (BN * D);
+    const int kl = kt * BN + r;
+    const bool valid = kl < p.seg_len;
+    const int nb = WIN ? win_origin(seg, p.win) + win_offset(valid ? kl : 0, p.win)
+                       : seg * p.seg_len + (valid ? kl : 0);   // key buffer row
+    const int n = p.kv_pos_base + nb;                        // its global row
+    int t = 0, h = 0, w = 0;
+    if (n < g.Nv) decode_pos(n, g, t, h, w);   // text rows: position (0, 0, 0), angles 0
+    float2 cs[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int id = threadIdx.x + 256 * i;
-        const int r = id >> 4, c = id & 15;
-        const int kl = kt * BN + r;
-        const bool valid = kl < p.seg_len;
-        const int nb = WIN ? win_origin(seg, p.win) + win_offset(valid ? kl : 0, p.win)
-                           : seg * p.seg_len + (valid ? kl : 0);   // key buffer row
-        const int n = p.kv_pos_base + nb;                    // its global row
-        uint4 raw = valid ? ld16(p.k + nb * row_stride + (long long)head * D + 8 * c) : make_uint4(0, 0, 0, 0);
-        int t = 0, h = 0, w = 0;
-        const bool text = n >= g.Nv;
-        if (!text) decode_pos(n, g, t, h, w);
-        *reinterpret_cast<uint4*>(out + r * D + 8 * c) = rope_chunk_f16(raw, c, t, h, w, g, p.table);
+    for (int i = 0; i < 4; ++i) cs[i] = p.table[pair_entry(4 * c + i, t, h, w, g)];
+    const uint16_t* src = p.k + nb * row_stride + 8 * c;
+    // Output row r of tile (head, seg, kt): ((head * n_segs + seg) * k_tiles + kt) * BN + r.
+    const long long head_stride = (long long)p.n_segs * p.k_tiles * BN * D;
+    uint16_t* dst = p.kt + ((long long)seg * p.k_tiles + kt) * (BN * D) + r * D + 8 * c;
+    for (int hb = 0; hb < p.heads; hb += 16) {
+        uint4 raw[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int hd = hb + h0 + 4 * k;
+            raw[k] = (valid && hd < p.heads) ? ld16(src + (long long)hd * D) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int hd = hb + h0 + 4 * k;
+            if (hd < p.heads) {
+                uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
+                    rotate_pair(x0, x1, cs[i]);
+                    wd[i] = pack_f16x2(x0, x1);
+                }
+                *reinterpret_cast<uint4*>(dst + hd * head_stride) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+            }
+        }
     }
 }
 
@@ -1112,7 +1138,7 @@ hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, c
     p.kv_pos_base = L.kv_pos_base;
     p.k_tiles = (L.kv_len + BN - 1) / BN;
     p.win = WinMap{};
-    const int blocks = heads * L.n_segs * p.k_tiles;
+    const int blocks = L.n_segs * p.k_tiles * (BN / 4);   // one wave per tile row
     hipLaunchKernelGGL(k_prep_kernel<false>, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
@@ -1130,7 +1156,7 @@ hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* tabl
     p.kv_pos_base = 0;
     p.k_tiles = (L + BN - 1) / BN;
     p.win = m;
-    const int blocks = heads * n_windows * p.k_tiles;
+    const int blocks = n_windows * p.k_tiles * (BN / 4);   // one wave per tile row
     hipLaunchKernelGGL(k_prep_kernel<true>, dim3(blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
