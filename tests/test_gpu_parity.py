@@ -344,3 +344,15 @@ def test_config_hunyuan_joint_sampled():
     rows = sample_rows(n, 118800, 3600, 512, 4003)
     got, ref = run_full(grid, heads, "bf16", 4000, n_text=n_text, split=HUN, rows=rows)
     assert_close(got, ref, "bf16", "33x45x80 + 256 text sampled rows")
+
+
+def test_reference_image_tokens_sampled():
+    """The Wan-14B 720p clip with 3 reference images of 4,096 tokens each concatenated into the
+    sequence (joint attention): N = 75,600 + 12,288 = 87,888, the shape whose attention costs 35 %
+    more than the clip alone.  The pages do not place these tokens in the grid, so they are
+    appended rows without rotation, as text is.  5 heads: one GPU's share of 40 over 8."""
+    grid, heads, n_text = (21, 45, 80), 5, 3 * 4096
+    n = 75600 + n_text
+    rows = sample_rows(n, 75600, 3600, 512, 5003)
+    got, ref = run_full(grid, heads, "bf16", 5000, n_text=n_text, rows=rows)
+    assert_close(got, ref, "bf16", "21x45x80 + 3 reference images (87,888 tokens) sampled rows")
