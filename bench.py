@@ -336,6 +336,32 @@ def main():
         win_ms = e0.elapsed_time(e1) / reps
         extras["window_7x10x13_ms"] = round(win_ms, 4)
         extras["window_7x10x13_TFLOPs"] = round(4.0 * n * L_win * HEADS * D / (win_ms * 1e-3) / 1e12, 2)
+        # The two long configurations at full size, timed the same way as the headline (they are
+        # parity cases on sampled rows elsewhere): the Wan-14B-shaped 720p clip (21 x 45 x 80,
+        # 40 heads) and HunyuanVideo's joint sequence (33 x 45 x 80 video rows + 256 appended text
+        # rows, 24 heads, split 16/56/56).  Synthetic N(0,1) bf16 inputs.
+        del fout, ws, rout, rws, fws, wws
+        for name, grid_l, heads_l, n_text_l, split_l in (("wan14b_720p", (21, 45, 80), 40, 0, SPLIT),
+                                                        ("hunyuan_joint", (33, 45, 80), 24, 256, (16, 56, 56))):
+            n_l = grid_l[0] * grid_l[1] * grid_l[2] + n_text_l
+            gl = torch.Generator(device=dev).manual_seed(SEED + 40)
+            ql, kl, vl = (torch.randn(n_l, heads_l, D, device=dev, generator=gl).to(torch.bfloat16)
+                          for _ in range(3))
+            wsl = torch.empty(fa.attn3d_workspace_bytes(grid_l, heads_l, n_text_l, D, split_l),
+                              dtype=torch.uint8, device=dev)
+            outl = torch.empty_like(ql)
+            fa.attn3d(ql, kl, vl, grid_l, n_text_l, split_l, THETA, out=outl, workspace=wsl)
+            reps_l = 3
+            e0.record(stream)
+            for _ in range(reps_l):
+                fa.attn3d(ql, kl, vl, grid_l, n_text_l, split_l, THETA, out=outl, workspace=wsl)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_l = e0.elapsed_time(e1) / reps_l
+            flop_l = 4.0 * n_l * n_l * heads_l * D
+            extras[f"{name}_ms"] = round(ms_l, 3)
+            extras[f"{name}_TFLOPs"] = round(flop_l / (ms_l * 1e-3) / 1e12, 2)
+            del ql, kl, vl, wsl, outl
         result["extras"] = extras
         eprint(f"extras: {extras}")
 
