@@ -67,6 +67,7 @@ constexpr int NBUF = 4;                          // tile j lives in K and V slot
 constexpr int PREF = 3;                          // step j fetches tile j + PREF
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
+constexpr int WIN_TABLE = 8192;                  // window mode: V row offsets kept in LDS (32 KB)
 constexpr float OVF_SUM = 0x1p64f;   // fast launch: a row sum this large (or not finite) flags the item
 constexpr float LAZY_LOG2 = 8.0f;  // move the offset when a row max exceeds it by more than this
 
@@ -185,6 +186,7 @@ template <bool FUSED, bool WIN>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     static_assert(!(FUSED && WIN), "window mode reads staged K");
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+    __shared__ uint32_t win_vrow[WIN ? WIN_TABLE : 1];   // window mode: byte offset of each V row
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
@@ -245,13 +247,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             const uint32_t vl = wl + V_LDS_BASE + slot * TILE_BYTES;
             const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
             if constexpr (WIN) {
-                // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
+                // Each lane addresses its own grid row from the head's base (total bytes < 2^32):
+                // from the item's table of row offsets, or by the window arithmetic past it.
+                const bool from_table = j * BN + BN <= WIN_TABLE;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = dr0 + 4 * i;
                     const int re = r < last ? r : last;
-                    const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
-                    dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+                    const uint32_t rb = from_table ? win_vrow[j * BN + re]
+                                                   : 2u * (uint32_t)(win0 + win_offset(j * BN + re, p.win)) * (uint32_t)row_stride;
+                    dma16(vhead, rb + vch2[i], vl + i * 1024);
                 }
             } else {
                 const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
@@ -295,6 +300,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
         };
 
         // ---- prologue -----------------------------------------------------------------------------
+        if constexpr (WIN) {
+            // The window's V row offsets, once per item: the tile copies then read them instead of
+            // doing two divisions per row and tile.  The previous item's copies were all issued
+            // before its last barrier, so the table is free to overwrite.
+            for (int li = tid; li < min(seg_len, WIN_TABLE); li += NTHREADS)
+                win_vrow[li] = 2u * (uint32_t)(win0 + win_offset(li, p.win)) * (uint32_t)row_stride;
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < PREF; ++j) {
             issue_tile(min(j, ntiles - 1), j);
@@ -601,6 +614,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 template <bool WIN>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
+    __shared__ uint32_t win_vrow[WIN ? WIN_TABLE : 1];   // window mode: byte offset of each V row
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
@@ -654,13 +668,16 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
             const uint32_t vl = wl + V_LDS_BASE + slot * TILE_BYTES;
             const int last = seg_len - 1 - j * BN;   // rows past the end repeat the last row
             if constexpr (WIN) {
-                // Each lane addresses its own grid row from the head's base (total bytes < 2^32).
+                // Each lane addresses its own grid row from the head's base (total bytes < 2^32):
+                // from the item's table of row offsets, or by the window arithmetic past it.
+                const bool from_table = j * BN + BN <= WIN_TABLE;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                     const int r = dr0 + 4 * i;
                     const int re = r < last ? r : last;
-                    const uint32_t n = (uint32_t)(win0 + win_offset(j * BN + re, p.win));
-                    dma16(vhead, 2u * (n * (uint32_t)row_stride + (uint32_t)v_chunk[i]), vl + i * 1024);
+                    const uint32_t rb = from_table ? win_vrow[j * BN + re]
+                                                   : 2u * (uint32_t)(win0 + win_offset(j * BN + re, p.win)) * (uint32_t)row_stride;
+                    dma16(vhead, rb + vch2[i], vl + i * 1024);
                 }
             } else {
                 const uint16_t* vt = vhead + (long long)(seg_base + j * BN) * row_stride;
@@ -676,6 +693,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
             for (int i = 0; i < 2; ++i) dma16(kt, k_src_off[i], kl + i * 1024);
         };
         // ---- prologue -----------------------------------------------------------------------------
+        if constexpr (WIN) {
+            // The window's V row offsets, once per item: the tile copies then read them instead of
+            // doing two divisions per row and tile.  The previous item's copies were all issued
+            // before its last barrier, so the table is free to overwrite.
+            for (int li = tid; li < min(seg_len, WIN_TABLE); li += NTHREADS)
+                win_vrow[li] = 2u * (uint32_t)(win0 + win_offset(li, p.win)) * (uint32_t)row_stride;
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < PREF; ++j) issue_tile(min(j, ntiles - 1), j);
 
