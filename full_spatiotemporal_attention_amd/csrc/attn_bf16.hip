@@ -340,20 +340,33 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             uint4 raw[8];
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) raw[ks] = ld16(qp + 16 * ks);
+            if (g.Nv > 0) {
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
-                uint32_t o[4];
+                for (int ks = 0; ks < 8; ++ks) {
+                    const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+                    uint32_t o[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int p0 = 8 * ks + i;
-                    const int base = p0 >= g2 ? bw : (p0 >= g1 ? bh : bt);
-                    const float2 cs = p.table[base + p0];
-                    float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
-                    rotate_pair(x0, x1, cs);
-                    o[i] = pack_f16x2(x0 * sc, x1 * sc);
+                    for (int i = 0; i < 4; ++i) {
+                        const int p0 = 8 * ks + i;
+                        const int base = p0 >= g2 ? bw : (p0 >= g1 ? bh : bt);
+                        const float2 cs = p.table[base + p0];
+                        float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
+                        rotate_pair(x0, x1, cs);
+                        o[i] = pack_f16x2(x0 * sc, x1 * sc);
+                    }
+                    qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
                 }
-                qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+            } else {
+                // No video rows (cross-attention): every angle is 0, so the rotation is the identity
+                // and no table entry is read.
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const uint32_t wd[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = pack_f16x2(bf16_lo(wd[i]) * sc, bf16_hi(wd[i]) * sc);
+                    qreg[ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+                }
             }
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
