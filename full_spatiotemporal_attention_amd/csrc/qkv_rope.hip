@@ -124,50 +124,62 @@ __global__ void __launch_bounds__(GTHREADS, 1) qkv_rope_bf16_kernel(QkvParams p)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[fb][tb][i] = 0.0f;
 
-    const int ksteps = C / GK;
+    const int ksteps = C / GK;   // C is a multiple of 128: ksteps is even and at least 2
+    // Stages 0 and 1 in flight; stage 0 must land before the first reads.
     issue_stage(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    issue_stage(1, 1);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 
+    // Operand double buffer; k16 step kk of a stage uses buffer kk & 1.
+    bf16x8_t a[2][2], b[2][4];
+    auto read_ops = [&](int buf, int stage, int kk) {
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb) a[buf][fb] = rd(a_rd[fb], stage, kk);
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) b[buf][tb] = rd(b_rd[tb], stage, kk);
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+        for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[buf][fb], b[buf][tb], acc[fb][tb], 0, 0, 0);
+    };
+    auto interleave = [&]() {   // 8 MFMAs with the 6 reads issued beside them
+#pragma unroll
+        for (int t = 0; t < 6; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    read_ops(0, 0, 0);
+
+    // Step ks (stage st): k16 steps 0-2 with the next one's operands read beside them; then the
+    // stage's reads and the next stage's copies are complete, the barrier releases the slot, the
+    // copies of stage ks+2 go into it, and k16 step 3 runs beside the reads of stage ks+1's first
+    // operands.  The barrier is crossed with 8 MFMAs in flight, and no step starts by waiting on
+    // LDS.  After the last step those reads fetch a stale slot (in bounds, never used): a branch
+    // around them would keep two operand sets live across it and spill.
     auto step = [&](auto stc, int ks) {
         constexpr int st = decltype(stc)::value;
-        if (ks + 1 < ksteps) issue_stage(ks + 1, st ^ 1);
-        // Operands of k16 step kk+1 are read while the MFMAs of step kk run.
-        bf16x8_t a[2][2], b[2][4];
 #pragma unroll
-        for (int fb = 0; fb < 2; ++fb) a[0][fb] = rd(a_rd[fb], st, 0);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) b[0][tb] = rd(b_rd[tb], st, 0);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < 4) {
-#pragma unroll
-                for (int fb = 0; fb < 2; ++fb) a[cur ^ 1][fb] = rd(a_rd[fb], st, kk + 1);
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb) b[cur ^ 1][tb] = rd(b_rd[tb], st, kk + 1);
-            }
-#pragma unroll
-            for (int fb = 0; fb < 2; ++fb)
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    acc[fb][tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][fb], b[cur][tb], acc[fb][tb], 0, 0, 0);
-            if (kk + 1 < 4) {
-#pragma unroll
-                for (int t = 0; t < 6; ++t) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int kk = 0; kk < 3; ++kk) {
+            read_ops((kk + 1) & 1, st, kk + 1);
+            mfmas(kk & 1);
+            interleave();
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
+        if (ks + 2 < ksteps) issue_stage(ks + 2, st);
+        read_ops(0, st ^ 1, 0);
+        mfmas(1);
+        interleave();
     };
-    // C is a multiple of 128 (heads x 128), so the k steps come in pairs.
     for (int ks = 0; ks < ksteps; ks += 2) {
         step(std::integral_constant<int, 0>{}, ks);
         step(std::integral_constant<int, 1>{}, ks + 1);
