@@ -966,13 +966,14 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                     for (int qb = 0; qb < 2; ++qb)
                         oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk][qb], oacc[db][qb], 0, 0, 0);
                 }
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
+            // Eight transposed reads (four V operands, eight MFMAs) ahead of their use.
+            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
 #pragma unroll
-            for (int t = 0; t < 28; ++t) {
+            for (int t = 0; t < 24; ++t) {
                 __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
 
             // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
