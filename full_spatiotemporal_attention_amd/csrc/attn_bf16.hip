@@ -590,27 +590,57 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
             }
         }
         // Copies issued by the last steps (repeats of the last tile) must land before the
-        // workgroup's LDS is released.
+        // workgroup's LDS is reused: every wave waits for its own, and the barrier for the others'.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
 
-        // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
+        // ---- epilogue: O / l -> bf16, through LDS to whole rows -------------------------------------
         const float l_tot = xhalf_sum(l_run);
         const float inv = 1.0f / l_tot;
         if (p.lse && q_valid && hh == 0)
             p.lse[(long long)q_row * p.heads + head] = m_run * 0.6931471805599453f + __logf(l_tot);
-        if (q_valid) {
-            uint16_t* op = p.out + q_row * row_stride + (long long)head * D;
+        {
+            // Wave w stages its 32 rows in LDS bytes 8 KB w ..: lane (l32, hh) holds channels
+            // 32 db + 8 grp + 4 hh .. +3 of row l32, i.e. half hh of 16-byte chunk 4 db + grp,
+            // stored at chunk (4 db + grp) ^ (l32 % 16) of the row.
+            const uint32_t sb = lds0 + wave * 8192;
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int grp = 0; grp < 4; ++grp) {
-                    const int d0 = 32 * db + 8 * grp + 4 * hh;
-                    uint2 u;
-                    u.x = pack_bf16x2(oacc[db][4 * grp + 0] * inv, oacc[db][4 * grp + 1] * inv);
-                    u.y = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
-                    *reinterpret_cast<uint2*>(op + d0) = u;
+                    typedef uint32_t st_u32x2_t __attribute__((ext_vector_type(2)));
+                    st_u32x2_t u;
+                    u[0] = pack_bf16x2(oacc[db][4 * grp + 0] * inv, oacc[db][4 * grp + 1] * inv);
+                    u[1] = pack_bf16x2(oacc[db][4 * grp + 2] * inv, oacc[db][4 * grp + 3] * inv);
+                    const uint32_t a = sb + l32 * 256 + 16 * ((4 * db + grp) ^ (l32 & 15)) + 8 * hh;
+                    *(__attribute__((address_space(3))) st_u32x2_t*)(uintptr_t)a = u;
                 }
+            // Lane L then writes 16-byte chunk L % 16 of rows 4 it + L / 16: 16 lanes per row.
+            const int qb0 = qt * BM + wave * 32;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const int r = 4 * it + (lane >> 4);
+                const int ql = qb0 + r;
+                const u32x4_t val = *(__attribute__((address_space(3))) const u32x4_t*)(uintptr_t)(
+                    sb + r * 256 + 16 * (pc ^ (r & 15)));
+                if (ql < q_len) {
+                    // Window mode: q, v and out share the row layout, so the item's table of V row
+                    // byte offsets gives the output row too.
+                    uint16_t* op;
+                    if constexpr (WIN) {
+                        const uint32_t rb = ql < WIN_TABLE ? win_vrow[ql]
+                                                           : 2u * (uint32_t)(win0 + win_offset(ql, p.win)) * (uint32_t)row_stride;
+                        op = p.out + (long long)head * D + 8 * pc + (rb >> 1);
+                    } else {
+                        op = p.out + (seg * q_len + ql) * row_stride + (long long)head * D + 8 * pc;
+                    }
+                    *reinterpret_cast<uint4*>(op) = make_uint4(val[0], val[1], val[2], val[3]);
+                }
+            }
         }
+        // The next item's copies overwrite the staging area.
+        __builtin_amdgcn_s_barrier();
     }  // item
 }
 
