@@ -49,36 +49,65 @@ __device__ __forceinline__ void store_chunk(float* p, const float (&x)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
 }
 
-template <typename T, int E>
+__device__ __forceinline__ void unpack_chunk(const uint4& u, float (&x)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_lo(w[i]);
+        x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+__device__ __forceinline__ void unpack_chunk(const uint4& u, float (&x)[4]) {
+    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+}
+
+// NP > 0: exactly NP parts.  Every part's chunk is requested before the log-sum-exps, so a thread
+// waits for one memory round trip, not two; the chunk registers are sized for NP.  NP = 0: any
+// p.n_parts up to kMaxMergeParts, chunks loaded after the weights (registers for 16 chunks would
+// halve the occupancy; with 8 parts the bf16 kernel would already drop to 5 waves per SIMD).
+template <typename T, int E, int NP>
 __global__ void __launch_bounds__(256) merge_kernel(MergeParams<T> p) {
+    constexpr int MP = NP > 0 ? NP : kMaxMergeParts;
+    const int n_parts = NP > 0 ? NP : p.n_parts;
     const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long rh = tid >> p.group_log2;
     const int c = (int)(tid & ((1 << p.group_log2) - 1));
     if (rh >= p.rows_heads) return;
-    float m = -INFINITY;
-    float l[kMaxMergeParts];
+    const bool active = c < p.chunks;
+    const long long off = rh * p.d + (long long)c * E;
+    uint4 raw[NP > 0 ? NP : 1];
+    if constexpr (NP > 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxMergeParts; ++i) {
-        l[i] = i < p.n_parts ? p.lse[i][rh] : -INFINITY;
+        for (int i = 0; i < NP; ++i)
+            if (active) raw[i] = *reinterpret_cast<const uint4*>(p.o[i] + off);
+    }
+    float m = -INFINITY;
+    float l[MP];
+#pragma unroll
+    for (int i = 0; i < MP; ++i) {
+        l[i] = i < n_parts ? p.lse[i][rh] : -INFINITY;
         m = fmaxf(m, l[i]);
     }
     float tot = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kMaxMergeParts; ++i) {
-        l[i] = (i < p.n_parts && m > -INFINITY) ? expf(l[i] - m) : 0.0f;
+    for (int i = 0; i < MP; ++i) {
+        l[i] = (i < n_parts && m > -INFINITY) ? expf(l[i] - m) : 0.0f;
         tot += l[i];
     }
     const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    if (c < p.chunks) {
+    if (active) {
         float acc[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-        const long long off = rh * p.d + (long long)c * E;
 #pragma unroll
-        for (int i = 0; i < kMaxMergeParts; ++i) {
-            if (i < p.n_parts) {
+        for (int i = 0; i < MP; ++i) {
+            if (i < n_parts) {
                 float x[E];
-                load_chunk(p.o[i] + off, x);
+                if constexpr (NP > 0)
+                    unpack_chunk(raw[i], x);
+                else
+                    load_chunk(p.o[i] + off, x);
                 const float w = l[i] * inv;
 #pragma unroll
                 for (int e = 0; e < E; ++e) acc[e] = fmaf(w, x[e], acc[e]);
@@ -106,8 +135,13 @@ hipError_t launch_merge(int n_parts, const T* const* o, const float* const* lse,
     p.out = out;
     p.lse_out = lse_out;
     const long long threads = rows_heads << p.group_log2;
-    const long long blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((merge_kernel<T, E>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    switch (n_parts) {
+        case 2: hipLaunchKernelGGL((merge_kernel<T, E, 2>), grid, dim3(256), 0, stream, p); break;
+        case 3: hipLaunchKernelGGL((merge_kernel<T, E, 3>), grid, dim3(256), 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((merge_kernel<T, E, 4>), grid, dim3(256), 0, stream, p); break;
+        default: hipLaunchKernelGGL((merge_kernel<T, E, 0>), grid, dim3(256), 0, stream, p); break;
+    }
     return hipGetLastError();
 }
 

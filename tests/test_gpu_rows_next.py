@@ -121,6 +121,28 @@ def test_merge_of_key_runs_equals_full_attention(dtype):
     assert float(np.abs(host_f64(lse) - rl2).max()) <= 1e-5
 
 
+@pytest.mark.parametrize("n_runs", [3, 5, 8])
+def test_merge_part_counts(n_runs):
+    # 2, 3 and 4 parts have kernels of their own; other counts take the general kernel.
+    grid, n_text, split, heads = (3, 5, 7), 6, WAN, 2
+    n = grid[0] * grid[1] * grid[2] + n_text
+    cuts = [round(i * n / n_runs) for i in range(n_runs)] + [n]
+    log(f"  merge of {n_runs} runs grid={grid} n_text={n_text} cuts={cuts} seed={7600 + n_runs}")
+    x, (q, k, v) = grid_inputs(grid, n_text, heads, "bf16", 7600 + n_runs, split)
+    parts = [fa.attn3d_partial(q, k[a:b].contiguous(), v[a:b].contiguous(), grid, q_begin=0,
+                               kv_begin=a, n_text=n_text, rope_split=split)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = fa.attn_merge(parts)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_partials_ref([(host_f64(a), host_f64(b)) for a, b in parts])
+    m_abs, m_rel = errors(host_f64(o), ro)
+    log(f"    merge vs oracle merge of the same partials: max_abs={m_abs:.3e} rel_l2={m_rel:.3e}")
+    assert m_abs <= 2 ** -8 * float(np.abs(ro).max()) + 1e-6   # one bf16 rounding of the output
+    assert float(np.abs(host_f64(lse) - rl).max()) <= 1e-5
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, grid, n_text, split, 10000.0)
+    assert_close(host_f64(o), ref, "bf16", f"merge of {n_runs} runs")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_merge_in_place_and_single_part(dtype):
     grid, split, heads = (3, 6, 6), WAN, 3
