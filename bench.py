@@ -107,7 +107,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip factorised and RoPE timings")
     ap.add_argument("--calibrate-copy", action="store_true",
