@@ -48,14 +48,17 @@ Readings where the pages are silent (each one is also listed in the design notes
 * RoPE pairs are interleaved, channels (off + 2j, off + 2j + 1) inside each contiguous range, ranges
   in the order t, h, w; pair j of an axis with range size d_a turns by pos * theta^(-2j / d_a)
   (each axis an independent 1D RoPE, theta = 10000); the turn is counter-clockwise:
-  (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).  PARITY UNPINNED for these conventions beyond the
+  (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).  The frequency ladder is pinned against an
+  independent per-axis rotary embedding (V-JEPA 2's, in `transformers`), both as a list and as the
+  angle each pair of the rotation turns by.  The pairing and the sign remain readings beyond the
   structural pins (block-diagonal form, norm preservation, relative-position invariance, identity
   at the origin): no page prints a rotated vector.
 * Text tokens, when present, come after all video tokens and are not rotated.
 * The factorised second stage uses the same rotated q and k and takes the first stage's output as
   its values.
-* Absolute attention outputs on random inputs: PARITY UNPINNED (no page prints one); pinned by the
-  special cases, invariants and an independent library routine in the tests.
+* Absolute attention outputs on random inputs: no page prints one, so the tests pin them by
+  special cases, invariants and an independent library routine (torch's scaled_dot_product_attention
+  in float64).
 * Cross-attention applies no rotation: the page gives 3D RoPE for the video self-attention and none
   for the text keys.  The log-sum-exp of a partial result is natural-log, over scaled scores
   s / sqrt(d).
@@ -186,7 +189,12 @@ def rope_pair_layout(split):
 
 
 def rope_frequencies(split, theta: float = 10000.0):
-    """Angular frequency of every pair, per axis: omega_{a,j} = theta^(-2j / d_a) (a reading)."""
+    """Angular frequency of every pair, per axis: omega_{a,j} = theta^(-2j / d_a).
+
+    Each axis range is an independent 1D RoPE over its own d_a channels ("FLUX's 2D RoPE plus a
+    time dimension", first page, "Position: RoPE in three dimensions"); the ladder is a reading,
+    pinned in the tests against an independent per-axis implementation.
+    """
     return [np.array([theta ** (-2.0 * j / da) for j in range(da // 2)], dtype=np.float64)
             for da in split]
 

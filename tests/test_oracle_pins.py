@@ -274,6 +274,77 @@ def test_rope_t_range_only_moves_with_t():
         assert np.abs(y[n, 0, :44] - y[same_hw[0], 0, :44]).max() > 1e-3
 
 
+# The frequency ladder.  No page prints a frequency: the first page calls the scheme "FLUX's 2D
+# RoPE plus a time dimension" ("A video model's architecture: spatiotemporal attention and the 3D
+# VAE", "Position: RoPE in three dimensions"), i.e. one independent 1D RoPE per axis range.  An
+# independent implementation of exactly that is importable here: the per-axis rotary embedding of
+# V-JEPA 2 in `transformers`, which rotates each axis range of D channels with its own ladder
+# over D.  Its channel pairing and frequency placement differ from the oracle's, so only the
+# ladder is compared, read back from the routine's output on unit vectors at position 1.
+
+def _vjepa2_axis_ladder(D):
+    """omega_k, k < D/2, of V-JEPA 2's rotary embedding of a D-channel axis range (theta 1e4).
+
+    Row k < D/2 of the routine's matrix at position 1 carries frequency index k on its diagonal
+    (cos) and in its pair partner's column (sin, signed by the pair side); the angle is then
+    atan2(sin, cos), unambiguous since every omega <= 1 < pi.
+    """
+    from transformers.models.vjepa2.modeling_vjepa2 import rotate_queries_or_keys
+    x = torch.eye(D, dtype=torch.float64).reshape(1, 1, D, D)     # token c holds unit vector e_c
+    pos = torch.ones(1, 1, D, dtype=torch.float64)
+    m = rotate_queries_or_keys(x, pos)[0, 0].T.numpy()             # m[r, c]: channel r of R e_c
+    om = np.empty(D // 2)
+    for kk in range(D // 2):
+        s = m[kk, kk - 1] if kk % 2 else -m[kk, kk + 1]
+        om[kk] = math.atan2(s, m[kk, kk])
+    return om
+
+
+LADDER_SPLITS = [(44, 42, 42), (16, 56, 56)]
+
+
+def check_ladder(freq_fn):
+    for split in LADDER_SPLITS:
+        freqs = freq_fn(split, 10000.0)
+        for axis, da in enumerate(split):
+            np.testing.assert_allclose(freqs[axis], _vjepa2_axis_ladder(da), rtol=1e-12, atol=0)
+
+
+def check_rope_turns_by_ladder(rope_fn):
+    # The rotation itself: a unit vector on the first channel of pair j of axis a, at the row whose
+    # coordinate on a is 1 and 0 on the other two, must turn by exactly the independent omega_{a,j}.
+    grid = (2, 2, 2)
+    for split in LADDER_SPLITS:
+        off = 0
+        for axis, da in enumerate(split):
+            row = (4, 2, 1)[axis]                       # (1,0,0), (0,1,0), (0,0,1) in flat order
+            ladder = _vjepa2_axis_ladder(da)
+            x = np.zeros((8, da // 2, 128))
+            for j in range(da // 2):
+                x[row, j, off + 2 * j] = 1.0
+            y = rope_fn(x, grid, 0, split, 10000.0)
+            for j in range(da // 2):
+                ang = math.atan2(y[row, j, off + 2 * j + 1], y[row, j, off + 2 * j])
+                assert ang == pytest.approx(ladder[j], rel=1e-12, abs=1e-15)
+            off += da
+
+
+def test_rope_frequency_ladder_matches_independent_axis_rope():
+    check_ladder(oracle.rope_frequencies)
+
+
+def test_rope_rotation_uses_the_independent_ladder():
+    check_rope_turns_by_ladder(oracle.rope3d_ref)
+
+
+def test_rope_ladder_probe_reads_known_endpoints():
+    # The probe itself, on closed forms: omega_0 = 1 for every range, and for D = 16 the ladder
+    # is 10^(-k/2) exactly (10000^(-2k/16)).
+    for D in (16, 42, 44, 56):
+        assert _vjepa2_axis_ladder(D)[0] == pytest.approx(1.0, abs=1e-15)
+    np.testing.assert_allclose(_vjepa2_axis_ladder(16), 10.0 ** (-np.arange(8) / 2.0), rtol=1e-12)
+
+
 # ------------------------------------------------------------------------------------------
 # Attention
 # ------------------------------------------------------------------------------------------
@@ -515,6 +586,54 @@ def test_planted_rope_mistakes_are_caught(mode):
 
 def test_planted_flat_order_mistake_is_caught():
     assert _fails(check_shards, _mut_positions_w_slowest)
+
+
+def _ladder_variant(mode):
+    """Frequency ladders with a planted mistake: the exponent without its factor 2, one exponent
+    over the whole head (pair index counted from the head's first pair), j counted from 1."""
+    def fn(split, theta=10000.0):
+        d = sum(split)
+        out, first = [], 0
+        for da in split:
+            j = np.arange(da // 2, dtype=np.float64)
+            if mode == "no_factor_2":
+                om = theta ** (-j / da)
+            elif mode == "global_exponent":
+                om = theta ** (-2.0 * (first + j) / d)
+            elif mode == "j_from_1":
+                om = theta ** (-2.0 * (j + 1) / da)
+            else:
+                om = theta ** (-2.0 * j / da)
+            out.append(om)
+            first += da // 2
+        return out
+    return fn
+
+
+def _rope_with_ladder(freq_fn):
+    """The oracle's rotation with its frequency ladder replaced."""
+    def fn(x, grid, n_text=0, split=(44, 42, 42), theta=10000.0, rows=None):
+        t, h, w, vid = so.token_positions(grid, n_text)
+        freqs = freq_fn(split, theta)
+        y = np.array(x, dtype=np.float64, copy=True)
+        for axis, j, c0 in so.rope_pair_layout(split):
+            phi = (t, h, w)[axis] * freqs[axis][j]
+            c = np.where(vid, np.cos(phi), 1.0)[:, None]
+            s = np.where(vid, np.sin(phi), 0.0)[:, None]
+            x0, x1 = x[:, :, c0], x[:, :, c0 + 1]
+            y[:, :, c0] = x0 * c - x1 * s
+            y[:, :, c0 + 1] = x0 * s + x1 * c
+        return y
+    return fn
+
+
+@pytest.mark.parametrize("mode", ["no_factor_2", "global_exponent", "j_from_1"])
+def test_planted_ladder_mistakes_are_caught(mode):
+    assert _fails(check_ladder, _ladder_variant(mode)), f"ladder mutant {mode} passed the pin"
+    assert _fails(check_rope_turns_by_ladder, _rope_with_ladder(_ladder_variant(mode)))
+    # the unmutated forms of the same helpers pass
+    assert not _fails(check_ladder, _ladder_variant("none"))
+    assert not _fails(check_rope_turns_by_ladder, _rope_with_ladder(_ladder_variant("none")))
 
 
 @pytest.mark.parametrize("mode", ["no_scale", "rope_on_v", "transposed"])
