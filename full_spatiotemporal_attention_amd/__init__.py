@@ -74,6 +74,31 @@ def _check_tensors(grid, n_text, *ts):
     return T, H, W, ref.shape[1], ref.shape[2]
 
 
+def _check_out(out, like, what="out"):
+    """A caller-supplied output must match `like` exactly: the C ABI only sees a pointer."""
+    if not isinstance(out, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if out.device != like.device or out.dtype != like.dtype:
+        raise ValueError(f"{what} must be on {like.device} with dtype {like.dtype}")
+    if out.shape != like.shape:
+        raise ValueError(f"{what} must have shape {tuple(like.shape)}, got {tuple(out.shape)}")
+    if not out.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return out
+
+
+def _check_rows_tensors(*ts):
+    """[rows, heads, d] GPU tensors sharing a device and dtype (cross and partial attention)."""
+    ref = ts[0]
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
+            raise ValueError("expected contiguous [rows, heads, d] GPU tensors")
+        if t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("tensors must share device and dtype")
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -100,6 +125,10 @@ def attn_factorized_workspace_bytes(grid, heads, d=128, rope_split=WAN_SPLIT,
 
 def _workspace(nbytes: int, device, workspace=None) -> torch.Tensor:
     if workspace is not None:
+        if not isinstance(workspace, torch.Tensor):
+            raise TypeError("workspace must be a torch tensor")
+        if workspace.device != torch.device(device) or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous tensor on {device}")
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
@@ -129,7 +158,7 @@ def attn3d(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensors(grid, n_text, q, out)
+        _check_out(out, q)
     nbytes = attn3d_workspace_bytes(grid, heads, n_text, d, rope_split, q.dtype)
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn3d_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads,
@@ -148,7 +177,7 @@ def attn3d_fused(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, o
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensors(grid, n_text, q, out)
+        _check_out(out, q)
     nbytes = int(lib.st_attn3d_fused_workspace_bytes(T, H, W, _lib.split_arg(rope_split)))
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn3d_fwd_fused(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
@@ -179,6 +208,12 @@ def attn3d_attend(q, v, grid, workspace, n_text=0, rope_split=WAN_SPLIT, out=Non
     T, H, W, heads, d = _check_tensors(grid, n_text, q, v)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
+    if workspace is None:
+        raise ValueError("attn3d_attend needs the workspace attn3d_stage filled")
+    nbytes = attn3d_workspace_bytes(grid, heads, n_text, d, rope_split, q.dtype)
+    workspace = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn3d_attend(q.data_ptr(), v.data_ptr(), T, H, W, int(n_text), heads, d,
                               _lib.split_arg(rope_split), _dtype_code(q), workspace.data_ptr(),
                               workspace.numel() * workspace.element_size(), out.data_ptr(),
@@ -194,6 +229,8 @@ def attn_factorized(q, k, v, grid, rope_split=WAN_SPLIT, theta=10000.0, out=None
     T, H, W, heads, d = _check_tensors(grid, 0, q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
     nbytes = attn_factorized_workspace_bytes(grid, heads, d, rope_split, q.dtype)
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn_factorized_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, heads, d,
@@ -212,7 +249,7 @@ def attn_window(q, k, v, grid, window, rope_split=WAN_SPLIT, theta=10000.0, out=
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check_tensors(grid, 0, q, out)
+        _check_out(out, q)
     win = _lib.split_arg(window)
     nbytes = int(lib.st_attn3d_window_workspace_bytes(T, H, W, heads, d, _lib.split_arg(rope_split), win,
                                                       _dtype_code(q)))
@@ -234,6 +271,8 @@ def rope3d_apply(x, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
     T, H, W, heads, d = _check_tensors(grid, n_text, x)
     if out is None:
         out = torch.empty_like(x)
+    else:
+        _check_out(out, x)
     nbytes = rope3d_table_bytes(grid, rope_split)
     ws = _workspace(nbytes, x.device, workspace)
     st = lib.st_rope3d_apply(x.data_ptr(), out.data_ptr(), T, H, W, int(n_text), heads, d,
@@ -246,11 +285,7 @@ def rope3d_apply(x, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
 def attn_cross(q, k, v, out=None, workspace=None) -> torch.Tensor:
     """Text cross-attention: softmax(q k^T / sqrt(d)) v, q [Nq, heads, d], k/v [Nkv, heads, d]."""
     lib = _lib.load()
-    for t in (q, k, v):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
-            raise ValueError("expected contiguous [rows, heads, d] GPU tensors")
-        if t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("tensors must share device and dtype")
+    _check_rows_tensors(q, k, v)
     if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
         raise ValueError("k and v must be [Nkv, heads, d] with the heads and d of q")
     n_q, heads, d = q.shape
@@ -258,6 +293,8 @@ def attn_cross(q, k, v, out=None, workspace=None) -> torch.Tensor:
     code = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
     nbytes = int(lib.st_attn_cross_workspace_bytes(n_q, n_kv, heads, d, code))
     ws = _workspace(nbytes, q.device, workspace)
     st = lib.st_attn_cross_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), n_q, n_kv, heads, d, code,
@@ -276,9 +313,7 @@ def attn3d_partial(q, k, v, grid, q_begin=0, kv_begin=0, n_text=0, rope_split=WA
     """
     lib = _lib.load()
     T, H, W = (int(x) for x in grid)
-    for t in (q, k, v):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous() or t.dim() != 3:
-            raise ValueError("expected contiguous [rows, heads, d] GPU tensors")
+    _check_rows_tensors(q, k, v)
     if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
         raise ValueError("k and v must be [Nkv, heads, d] with the heads and d of q")
     q_count, heads, d = q.shape
@@ -304,16 +339,25 @@ def attn_merge(parts, out=None, lse_out=None):
     if not parts:
         raise ValueError("no parts")
     o0, l0 = parts[0]
+    if not isinstance(o0, torch.Tensor) or o0.dim() != 3 or o0.device.type != "cuda":
+        raise ValueError("parts must be [rows, heads, d] GPU tensors")
     n_rows, heads, d = o0.shape
     for o, l in parts:
-        if o.shape != o0.shape or o.dtype != o0.dtype or not o.is_contiguous():
-            raise ValueError("parts must share shape and dtype")
-        if l.shape != (n_rows, heads) or l.dtype != torch.float32 or not l.is_contiguous():
-            raise ValueError("lse parts must be contiguous float32 [rows, heads]")
+        if not isinstance(o, torch.Tensor) or not isinstance(l, torch.Tensor):
+            raise TypeError("parts must be (out, lse) pairs of torch tensors")
+        if o.shape != o0.shape or o.dtype != o0.dtype or o.device != o0.device or not o.is_contiguous():
+            raise ValueError("parts must share shape, dtype and device, and be contiguous")
+        if (l.shape != (n_rows, heads) or l.dtype != torch.float32 or l.device != o0.device
+                or not l.is_contiguous()):
+            raise ValueError("lse parts must be contiguous float32 [rows, heads] on the parts' device")
     if out is None:
         out = torch.empty_like(o0)
+    else:
+        _check_out(out, o0)
     if lse_out is None:
         lse_out = torch.empty_like(l0)
+    else:
+        _check_out(lse_out, l0, "lse_out")
     n = len(parts)
     optr = (ctypes.c_void_p * n)(*[o.data_ptr() for o, _ in parts])
     lptr = (ctypes.c_void_p * n)(*[l.data_ptr() for _, l in parts])
@@ -335,11 +379,15 @@ def qkv_rope(x, w, grid, bias=None, n_text=0, rope_split=WAN_SPLIT, theta=10000.
     for t in (x, w) + ((bias,) if bias is not None else ()):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
             raise ValueError("expected contiguous GPU tensors")
-        if t.dtype != x.dtype:
-            raise ValueError("x, w and bias must share a dtype")
+        if t.dtype != x.dtype or t.device != x.device:
+            raise ValueError("x, w and bias must share a dtype and device")
+    if x.dim() != 2:
+        raise ValueError("x must be [N, C]")
     n, c = x.shape
     if w.shape != (3 * c, c) or c % d:
         raise ValueError("w must be [3C, C] and C a multiple of the head dim")
+    if bias is not None and bias.shape != (3 * c,):
+        raise ValueError("bias must be [3C]")
     heads = c // d
     code = _dtype_code(x)
     q = torch.empty((n, heads, d), dtype=x.dtype, device=x.device)

@@ -85,6 +85,47 @@ __global__ void __launch_bounds__(256) rope_apply_bf16_kernel(const uint16_t* x,
     }
 }
 
+// bf16, any d % 8 == 0 other than 128: one wave per row, lane l takes the row's 16-byte chunks
+// l, l + 64, ... (chunk ci is chunk ci % (d/8) of head ci / (d/8)); each chunk looks up its own
+// four table entries.  All of a pass's loads are issued before its stores, as above.
+__global__ void __launch_bounds__(256) rope_apply_bf16_any_kernel(const uint16_t* x, uint16_t* y,
+                                                                  RopeGeom g, int N, int heads,
+                                                                  int d,
+                                                                  const float2* __restrict__ table) {
+    const int lane = threadIdx.x & 63;
+    const int cpr = d >> 3;                 // chunks per head
+    const int chunks = heads * cpr;         // chunks per row
+    const int waves = gridDim.x * 4;
+    for (int n = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (int)(threadIdx.x >> 6)); n < N; n += waves) {
+        int t = 0, h = 0, w = 0;
+        if (n < g.Nv) decode_pos(n, g, t, h, w);
+        const long long rb = (long long)n * chunks * 8;
+        for (int cb = 0; cb < chunks; cb += 256) {
+            uint4 raw[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int ci = cb + lane + 64 * k;
+                if (ci < chunks) raw[k] = *reinterpret_cast<const uint4*>(x + rb + 8ll * ci);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int ci = cb + lane + 64 * k;
+                if (ci < chunks) {
+                    const int c = ci % cpr;
+                    uint32_t wds[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+#pragma unroll
+                    for (int pi = 0; pi < 4; ++pi) {
+                        float x0 = bf16_lo(wds[pi]), x1 = bf16_hi(wds[pi]);
+                        rotate_pair(x0, x1, table[pair_entry(4 * c + pi, t, h, w, g)]);
+                        wds[pi] = pack_bf16x2(x0, x1);
+                    }
+                    *reinterpret_cast<uint4*>(y + rb + 8ll * ci) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                }
+            }
+        }
+    }
+}
+
 // fp32: one thread handles one pair (8 bytes).
 __global__ void __launch_bounds__(256) rope_apply_f32_kernel(const float* x,
                                                              float* y, RopeGeom g,
@@ -116,13 +157,16 @@ static int stream_grid(long long work, int threads) {
 
 hipError_t launch_rope_apply_bf16(const uint16_t* x, uint16_t* y, const RopeGeom& g, int N,
                                   int heads, int d, const float2* table, hipStream_t stream) {
-    if (d != 128) return hipErrorInvalidValue;
     // One wave per row, four rows per workgroup, up to 64 rows per wave.
     long long blocks = ((long long)N + 3) / 4;
     const long long cap = 256LL * 128;
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(rope_apply_bf16_kernel, dim3((int)blocks), dim3(256), 0, stream,
-                       x, y, g, N, heads, table);
+    if (d == 128)
+        hipLaunchKernelGGL(rope_apply_bf16_kernel, dim3((int)blocks), dim3(256), 0, stream,
+                           x, y, g, N, heads, table);
+    else
+        hipLaunchKernelGGL(rope_apply_bf16_any_kernel, dim3((int)blocks), dim3(256), 0, stream,
+                           x, y, g, N, heads, d, table);
     return hipGetLastError();
 }
 

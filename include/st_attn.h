@@ -67,11 +67,14 @@ typedef enum st_dtype {
 } st_dtype;
 
 /* ---------------------------------------------------------------------------------------------
- * RoPE angle table.  One (cos, sin) float pair per axis position and pair index, built in fp64
- * and stored as fp32: [T][d_t/2], then [H][d_h/2], then [W][d_w/2], then one identity entry
- * (1, 0) used by text rows.  Depends only on the grid, the split and theta, so a caller that runs
- * many layers on one grid can build it once.  The attention entry points build their own copy
- * in their workspace.
+ * RoPE angle table ("A video model's architecture: spatiotemporal attention and the 3D VAE",
+ * "Position: RoPE in three dimensions": each axis range is its own 1D RoPE, so pair j of a range
+ * of d_a channels at coordinate p turns by p * theta^(-2j / d_a)).  One (cos, sin) float pair per
+ * axis position and pair index, built in fp64 and rounded once to fp32: [T][d_t/2], then
+ * [H][d_h/2], then [W][d_w/2], then one identity entry (1, 0) used by text rows.  Depends only on
+ * the grid, the split and theta, so a caller that runs many layers on one grid can build it once.
+ * The attention entry points build their own copy in their workspace.  The table is written by
+ * one launch on `stream`; `table` is caller-owned device memory, 256-byte aligned.
  * ------------------------------------------------------------------------------------------- */
 
 /* Bytes of the table for this grid and split; 0 if the arguments are invalid. */
@@ -181,9 +184,15 @@ st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int 
                                size_t ws_bytes, void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Stand-alone 3D RoPE: y = R_3D(t, h, w) x for every row (text rows copied unchanged).
+ * Stand-alone 3D RoPE: y = R_3D(t, h, w) x for every row (text rows copied unchanged): the
+ * block-diagonal rotation of "CogVideoX Architecture: ...", section "3. 3D Rotary Position
+ * Embeddings (3D RoPE)", with the head cut into t, h and w ranges as in "A video model's
+ * architecture: spatiotemporal attention and the 3D VAE", "Position: RoPE in three dimensions".
  * x and y: [N][heads][d]; y == x (in place) is allowed, other overlaps are not.  ST_BF16 needs
- * d % 8 == 0, ST_F32 needs d even.  Workspace: st_rope3d_table_bytes bytes.
+ * d % 8 == 0 (each 16-byte chunk holds four whole pairs; d == 128 takes a faster kernel), ST_F32
+ * needs d even.  bf16 results are rotated in fp32 and rounded once.  Workspace (caller-owned,
+ * 256-byte aligned): st_rope3d_table_bytes bytes; the angle table is rebuilt into it on every
+ * call.  Two launches (table, rotation) on `stream`; all arguments are checked first.
  * ------------------------------------------------------------------------------------------- */
 st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_text, int heads,
                           int d, const int rope_split[3], float theta, st_dtype dtype,

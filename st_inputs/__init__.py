@@ -22,6 +22,7 @@ __all__ = [
     "QKV",
     "make_qkv",
     "sample_rows",
+    "sample_rows_per_head",
 ]
 
 
@@ -136,3 +137,10 @@ def sample_rows(n_tokens: int, n_video: int, tokens_per_frame: int, n_samples: i
     need = max(0, min(n_samples - len(chosen), rest.size))
     extra = g.choice(rest, size=need, replace=False)
     return np.sort(np.concatenate([np.array(chosen, dtype=np.int64), extra.astype(np.int64)]))
+
+
+def sample_rows_per_head(n_tokens: int, n_video: int, tokens_per_frame: int, n_samples: int,
+                         seed: int, head: int, tile_rows: int = 256) -> np.ndarray:
+    """The rows checked for one head: ``sample_rows`` with the seed ``seed + head``, so that each
+    head is compared on its own draw (the edge rows are in every head's set)."""
+    return sample_rows(n_tokens, n_video, tokens_per_frame, n_samples, seed + head, tile_rows)

@@ -223,6 +223,8 @@ def test_rope_apply_rejects_invalid_arguments(lib):
     assert f(y=None) == ST_ERR_NULL
     assert f(ws=None) == ST_ERR_NULL
     assert f(d=126, split=(42, 42, 42)) == ST_ERR_UNSUPPORTED         # bf16 needs d % 8 == 0
+    assert f(d=60, split=(20, 20, 20)) == ST_ERR_UNSUPPORTED
+    assert f(d=60, split=(20, 20, 20), dtype=1, ws=None) == ST_ERR_NULL  # f32 takes even d
     assert f(split=(44, 44, 42)) == ST_ERR_SPLIT
     assert f(ws_bytes=8) == ST_ERR_WORKSPACE
     assert f(y=Q + 256) == ST_ERR_ALIAS
@@ -246,6 +248,28 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(72, 2, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.attn3d(x, x, x, (3, 4, 6))
+
+
+def test_python_binding_checks_caller_outputs():
+    # The C ABI sees raw pointers, so the binding must refuse a caller-supplied output that does
+    # not match: wrong shape, dtype, device or layout (checked here on CPU tensors; the GPU tests
+    # call every wrapper with such outputs).
+    import torch
+    import full_spatiotemporal_attention_amd as fa
+    like = torch.zeros(72, 2, 128, dtype=torch.bfloat16)
+    fa._check_out(torch.empty_like(like), like)
+    with pytest.raises(ValueError):
+        fa._check_out(torch.empty(71, 2, 128, dtype=torch.bfloat16), like)
+    with pytest.raises(ValueError):
+        fa._check_out(torch.empty(72, 2, 128, dtype=torch.float32), like)
+    with pytest.raises(ValueError):
+        fa._check_out(torch.empty(2, 72, 128, dtype=torch.bfloat16).transpose(0, 1), like)
+    with pytest.raises(TypeError):
+        fa._check_out(None, like)
+    with pytest.raises(ValueError):
+        fa._check_rows_tensors(like, like.float())
+    with pytest.raises(ValueError):
+        fa._workspace(256, "cpu", torch.empty(10, dtype=torch.uint8))
 
 
 LSE = 0x600000000

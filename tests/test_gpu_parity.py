@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import full_spatiotemporal_attention_amd as fa
-from st_inputs import make_qkv, sample_rows
+from st_inputs import QKV, make_qkv, sample_rows, sample_rows_per_head
 from parity_util import assert_close, errors, host_f64, log, to_device
 
 pytestmark = pytest.mark.gpu
@@ -46,6 +46,30 @@ def run_full(grid, heads, dtype, seed, n_text=0, split=WAN, rows=None, head_subs
                                     heads=hsel)
     got = got[:, hsel] if rows is None else got[rows][:, hsel]
     return got, ref
+
+
+def run_full_sampled(grid, heads, seed, row_seed, n_text=0, split=WAN, n_rows=512, **gen):
+    """Full bf16 attention on the GPU, then the oracle on n_rows query rows per head, each head
+    with its own seeded sample (seed row_seed + head; edge rows always included).  Returns the
+    checked elements of every head, concatenated."""
+    T, H, W = grid
+    nv = T * H * W
+    n = nv + n_text
+    log(f"  full attention grid={grid} n_text={n_text} heads={heads} split={split} seed={seed} "
+        f"rows={n_rows} per head (seeds {row_seed}..{row_seed + heads - 1})")
+    x = make_qkv(n, heads, 128, seed, "bf16", **gen)
+    q, k, v = to_device(x)
+    out = fa.attn3d(q, k, v, grid, n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    del q, k, v, out
+    gs, rs = [], []
+    for hd in range(heads):
+        rows = sample_rows_per_head(n, nv, H * W, n_rows, row_seed, hd)
+        rs.append(oracle.full_attention_ref(x.q, x.k, x.v, grid, n_text, split, 10000.0, rows=rows,
+                                            heads=[hd]).ravel())
+        gs.append(got[rows, hd].ravel())
+    return np.concatenate(gs), np.concatenate(rs)
 
 
 # ------------------------------------------------------------------------------------------
@@ -92,6 +116,23 @@ def test_rope_apply(dtype, grid, n_text, heads, split):
     # text rows pass through unchanged
     np.testing.assert_array_equal(y[T * H * W:], host_f64(q)[T * H * W:])
     # in place gives the same values
+    y2 = host_f64(fa.rope3d_apply(q, grid, n_text=n_text, rope_split=split, out=q))
+    np.testing.assert_array_equal(y2, y)
+
+
+@pytest.mark.parametrize("d,split,heads,n_text", [(64, (20, 22, 22), 3, 4), (96, (32, 32, 32), 5, 0),
+                                                  (8, (4, 2, 2), 70, 3), (256, (88, 84, 84), 2, 1)])
+def test_rope_apply_bf16_other_head_dims(d, split, heads, n_text):
+    # bf16 serves every d % 8 == 0, not only 128 (a generic kernel, chunk by chunk).
+    grid = (3, 4, 5)
+    n = 60 + n_text
+    log(f"  rope_apply bf16 d={d} split={split} heads={heads} n_text={n_text}")
+    x = make_qkv(n, heads, d, 78, "bf16")
+    q, _, _ = to_device(x)
+    y = host_f64(fa.rope3d_apply(q, grid, n_text=n_text, rope_split=split))
+    ref = oracle.rope3d_ref(x.q, grid, n_text, split)
+    assert (np.abs(y - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6).all()
+    np.testing.assert_array_equal(y[60:], host_f64(q)[60:])
     y2 = host_f64(fa.rope3d_apply(q, grid, n_text=n_text, rope_split=split, out=q))
     np.testing.assert_array_equal(y2, y)
 
@@ -261,6 +302,64 @@ def test_deterministic():
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+def test_deterministic_fast_launch():
+    # 16,384 tokens x 2 heads is past the fast-launch threshold: the headline kernel (and its
+    # guard launch) must give the same bits on every run, and so must the factorised path.
+    n = 8 * 32 * 64
+    log(f"  determinism of the fast launch grid={FAST_GRID} heads=2")
+    x = make_qkv(n, 2, 128, 402, "bf16")
+    q, k, v = to_device(x)
+    outs = [fa.attn3d(q, k, v, FAST_GRID).view(torch.int16).clone() for _ in range(3)]
+    facts = [fa.attn_factorized(q, k, v, FAST_GRID).view(torch.int16).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    assert torch.equal(facts[0], facts[1]) and torch.equal(facts[0], facts[2])
+
+
+def _with_non_finite(x, which, row, head, value):
+    """A copy of bf16 inputs with channel 3 of one (row, head) of q, k or v set to NaN or +-inf."""
+    y = QKV(q=x.q.copy(), k=x.k.copy(), v=x.v.copy(), dtype=x.dtype, q_bits=x.q_bits.copy(),
+            k_bits=x.k_bits.copy(), v_bits=x.v_bits.copy())
+    bits = 0x7FC0 if math.isnan(value) else (0x7F80 if value > 0 else 0xFF80)
+    getattr(y, which)[row, head, 3] = value
+    getattr(y, which + "_bits")[row, head, 3] = bits
+    return y
+
+
+@pytest.mark.parametrize("grid,heads", [((5, 9, 11), 2), (FAST_GRID, 2)])
+def test_non_finite_inputs_give_non_finite_rows(grid, heads):
+    """A NaN or an infinity in the inputs ends as non-finite output rows, never as a hang or a
+    silently finite row: a NaN (or +inf) in query row r spoils exactly row r of its head, and a NaN
+    in one key or value row spoils every row of its head.  Everything else matches the clean run
+    bit for bit.  Both the running-max kernel (small grid) and the fast launch are exercised."""
+    T, H, W = grid
+    n = T * H * W
+    x = make_qkv(n, heads, 128, 403, "bf16")
+    q, k, v = to_device(x)
+    clean = host_f64(fa.attn3d(q, k, v, grid))
+    r = n // 3
+    for which, value in (("q", float("nan")), ("q", float("inf")), ("k", float("nan")), ("v", float("nan"))):
+        log(f"  non-finite input grid={grid} {which}[{r}, 1, 3] = {value}")
+        y = _with_non_finite(x, which, r, 1, value)
+        qy, ky, vy = to_device(y)
+        got = host_f64(fa.attn3d(qy, ky, vy, grid))
+        torch.cuda.synchronize()
+        bad = ~np.isfinite(got)
+        if which == "q":
+            assert bad[r, 1].all()
+            bad[r, 1] = False
+        else:
+            assert bad[:, 1].all()
+            bad[:, 1] = False
+        assert not bad.any()
+        # the untouched head is bit-identical to the clean run
+        np.testing.assert_array_equal(got[:, 0], clean[:, 0])
+        if which == "q":
+            keep = np.ones(n, bool)
+            keep[r] = False
+            np.testing.assert_array_equal(got[keep, 1], clean[keep, 1])
+
+
 # ------------------------------------------------------------------------------------------
 # Factorised
 # ------------------------------------------------------------------------------------------
@@ -308,16 +407,14 @@ def test_config_wan13b_17f_all_rows_two_heads_and_sample():
     grid, heads = (5, 30, 52), 12
     got, ref = run_full(grid, heads, "bf16", 1000, head_subset=[0, 11])
     assert_close(got, ref, "bf16", "5x30x52 all rows, heads 0 and 11")
-    rows = sample_rows(7800, 7800, 1560, 512, 1003)
-    got, ref = run_full(grid, heads, "bf16", 1000, rows=rows)
-    assert_close(got, ref, "bf16", "5x30x52 sampled rows, 12 heads")
+    got, ref = run_full_sampled(grid, heads, 1000, 1003)
+    assert_close(got, ref, "bf16", "5x30x52 sampled rows per head, 12 heads")
 
 
 def test_config_wan13b_81f_sampled():
     grid, heads = (21, 30, 52), 12
-    rows = sample_rows(32760, 32760, 1560, 512, 2003)
-    got, ref = run_full(grid, heads, "bf16", 2000, rows=rows)
-    assert_close(got, ref, "bf16", "21x30x52 sampled rows")
+    got, ref = run_full_sampled(grid, heads, 2000, 2003)
+    assert_close(got, ref, "bf16", "21x30x52 sampled rows per head")
 
 
 def test_config_wan13b_81f_factorized_sampled():
@@ -325,25 +422,26 @@ def test_config_wan13b_81f_factorized_sampled():
     x = make_qkv(32760, heads, 128, 2000, "bf16")
     q, k, v = to_device(x)
     got = host_f64(fa.attn_factorized(q, k, v, grid))
-    rows = sample_rows(32760, 32760, 1560, 512, 2003)
-    log("  factorised 21x30x52 sampled rows")
-    ref = oracle.factorized_ref(x.q, x.k, x.v, grid, rows=rows)
-    assert_close(got[rows], ref, "bf16", "21x30x52 factorised sampled")
+    log("  factorised 21x30x52 sampled rows per head")
+    gs, rs = [], []
+    for hd in range(heads):
+        rows = sample_rows_per_head(32760, 32760, 1560, 512, 2003, hd)
+        sl = slice(hd, hd + 1)
+        rs.append(oracle.factorized_ref(x.q[:, sl], x.k[:, sl], x.v[:, sl], grid, rows=rows).ravel())
+        gs.append(got[rows, hd].ravel())
+    assert_close(np.concatenate(gs), np.concatenate(rs), "bf16", "21x30x52 factorised sampled per head")
 
 
 def test_config_wan14b_720p_sampled():
     grid, heads = (21, 45, 80), 40
-    rows = sample_rows(75600, 75600, 3600, 512, 3003)
-    got, ref = run_full(grid, heads, "bf16", 3000, rows=rows, row_scale=(0.5, 2.0))
-    assert_close(got, ref, "bf16", "21x45x80 sampled rows, row-scaled inputs")
+    got, ref = run_full_sampled(grid, heads, 3000, 3003, row_scale=(0.5, 2.0))
+    assert_close(got, ref, "bf16", "21x45x80 sampled rows per head, row-scaled inputs")
 
 
 def test_config_hunyuan_joint_sampled():
     grid, heads, n_text = (33, 45, 80), 24, 256
-    n = 118800 + n_text
-    rows = sample_rows(n, 118800, 3600, 512, 4003)
-    got, ref = run_full(grid, heads, "bf16", 4000, n_text=n_text, split=HUN, rows=rows)
-    assert_close(got, ref, "bf16", "33x45x80 + 256 text sampled rows")
+    got, ref = run_full_sampled(grid, heads, 4000, 4003, n_text=n_text, split=HUN)
+    assert_close(got, ref, "bf16", "33x45x80 + 256 text sampled rows per head")
 
 
 def test_reference_image_tokens_sampled():
@@ -352,7 +450,45 @@ def test_reference_image_tokens_sampled():
     more than the clip alone.  The pages do not place these tokens in the grid, so they are
     appended rows without rotation, as text is.  5 heads: one GPU's share of 40 over 8."""
     grid, heads, n_text = (21, 45, 80), 5, 3 * 4096
-    n = 75600 + n_text
-    rows = sample_rows(n, 75600, 3600, 512, 5003)
-    got, ref = run_full(grid, heads, "bf16", 5000, n_text=n_text, rows=rows)
-    assert_close(got, ref, "bf16", "21x45x80 + 3 reference images (87,888 tokens) sampled rows")
+    got, ref = run_full_sampled(grid, heads, 5000, 5003, n_text=n_text)
+    assert_close(got, ref, "bf16", "21x45x80 + 3 reference images (87,888 tokens) sampled rows per head")
+
+
+# ------------------------------------------------------------------------------------------
+# Binding: caller-supplied outputs are checked before anything is launched
+# ------------------------------------------------------------------------------------------
+
+def test_binding_refuses_mismatched_outputs():
+    grid = (3, 4, 6)
+    x = make_qkv(72, 2, 128, 700, "bf16")
+    q, k, v = to_device(x)
+    dev = q.device
+    bad = [torch.full((71, 2, 128), 7.0, dtype=torch.bfloat16, device=dev),          # shape
+           torch.full((72, 2, 128), 7.0, dtype=torch.float32, device=dev),           # dtype
+           torch.full((2, 72, 128), 7.0, dtype=torch.bfloat16, device=dev).transpose(0, 1)]  # layout
+    ws = fa.attn3d_stage(k, grid)
+    calls = [
+        lambda o: fa.attn3d(q, k, v, grid, out=o),
+        lambda o: fa.attn3d_fused(q, k, v, grid, out=o),
+        lambda o: fa.attn3d_attend(q, v, grid, ws, out=o),
+        lambda o: fa.attn_factorized(q, k, v, grid, out=o),
+        lambda o: fa.attn_window(q, k, v, grid, (1, 2, 3), out=o),
+        lambda o: fa.rope3d_apply(q, grid, out=o),
+        lambda o: fa.attn_cross(q, k[:16], v[:16], out=o),
+    ]
+    for call in calls:
+        for o in bad:
+            with pytest.raises(ValueError):
+                call(o)
+        call(torch.empty_like(q))                   # a matching output is accepted
+    parts = fa.attn3d_partial(q, k, v, grid)
+    with pytest.raises(ValueError):
+        fa.attn_merge([parts], out=bad[0])
+    with pytest.raises(ValueError):
+        fa.attn_merge([parts], lse_out=torch.empty(72, 2, dtype=torch.bfloat16, device=dev))
+    with pytest.raises(ValueError):
+        fa.attn_merge([parts], lse_out=torch.empty(71, 2, dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    # nothing was written through a refused output
+    for o in bad:
+        assert bool((o == 7.0).all())
