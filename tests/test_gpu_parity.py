@@ -329,9 +329,9 @@ def _with_non_finite(x, which, row, head, value):
 @pytest.mark.parametrize("grid,heads", [((5, 9, 11), 2), (FAST_GRID, 2)])
 def test_non_finite_inputs_give_non_finite_rows(grid, heads):
     """A NaN or an infinity in the inputs ends as non-finite output rows, never as a hang or a
-    silently finite row: a NaN (or +inf) in query row r spoils exactly row r of its head, and a NaN
-    in one key or value row spoils every row of its head.  Everything else matches the clean run
-    bit for bit.  Both the running-max kernel (small grid) and the fast launch are exercised."""
+    silently finite row: a NaN (or +inf) in query row r spoils exactly row r of its head, a NaN in
+    one key row spoils every row of its head, and a NaN in channel c of one value row spoils channel
+    c of every row of its head.  Everything else matches the clean run bit for bit.  Both the running-max kernel (small grid) and the fast launch are exercised."""
     T, H, W = grid
     n = T * H * W
     x = make_qkv(n, heads, 128, 403, "bf16")
@@ -348,9 +348,13 @@ def test_non_finite_inputs_give_non_finite_rows(grid, heads):
         if which == "q":
             assert bad[r, 1].all()
             bad[r, 1] = False
-        else:
+        elif which == "k":
             assert bad[:, 1].all()
             bad[:, 1] = False
+        else:
+            # a value channel only reaches the same output channel
+            assert bad[:, 1, 3].all()
+            bad[:, 1, 3] = False
         assert not bad.any()
         # the untouched head is bit-identical to the clean run
         np.testing.assert_array_equal(got[:, 0], clean[:, 0])
@@ -358,6 +362,8 @@ def test_non_finite_inputs_give_non_finite_rows(grid, heads):
             keep = np.ones(n, bool)
             keep[r] = False
             np.testing.assert_array_equal(got[keep, 1], clean[keep, 1])
+        if which == "v":
+            np.testing.assert_array_equal(got[:, 1, :3], clean[:, 1, :3])
 
 
 # ------------------------------------------------------------------------------------------
