@@ -16,6 +16,7 @@ __all__ = [
     "StError",
     "attn3d",
     "attn3d_fused",
+    "attn3d_noalloc",
     "attn3d_stage",
     "attn3d_attend",
     "attn_factorized",
@@ -166,6 +167,23 @@ def attn3d(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=Non
                            ws.data_ptr(), ws.numel() * ws.element_size(), out.data_ptr(),
                            _stream(q.device))
     _lib.check("st_attn3d_fwd", st)
+    return out
+
+
+def attn3d_noalloc(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0, out=None) -> torch.Tensor:
+    """attn3d without a workspace: the library's static per-device scratch (see the C header for
+    its size limit and the race between overlapping calls on one GPU).  With ``out`` given, the
+    call allocates nothing."""
+    lib = _lib.load()
+    T, H, W, heads, d = _check_tensors(grid, n_text, q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_out(out, q)
+    st = lib.st_attn3d_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
+                                   heads, d, _lib.split_arg(rope_split), float(theta), _dtype_code(q),
+                                   out.data_ptr(), _stream(q.device))
+    _lib.check("st_attn3d_fwd_noalloc", st)
     return out
 
 

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "st_internal.h"
 
 namespace st {
@@ -195,6 +197,34 @@ bool ws_overlaps_tensors(const void* ws, size_t ws_bytes, size_t tensor_bytes, c
     return false;
 }
 
+// ---- scratch of the allocation-free entry point ------------------------------------------------
+// Every GPU the library runs on holds one copy of `scratch` (ST_NOALLOC_SCRATCH_BYTES, from module
+// load until the process ends).  In host code the array's name is only a stand-in: its device
+// address on each GPU comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is ever handed to kernels.
+static __device__ __align__(256) uint8_t scratch[ST_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (null and the HIP error on failure).
+void* scratch_on_current_device(hipError_t* err) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) { *err = e; return nullptr; }
+    if (dev < 0 || dev >= kMaxDevices) { *err = hipErrorInvalidDevice; return nullptr; }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) { *err = e != hipSuccess ? e : hipErrorInvalidSymbol; return nullptr; }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *err = hipSuccess;
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -309,6 +339,28 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int 
     e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
                             table, g, heads, d, f32_layout(1, (int)n, 0, 1, (int)n, 0, 1), stream);
     return e == hipSuccess ? ST_OK : hip_fail(e);
+}
+
+size_t st_attn3d_noalloc_scratch_bytes(void) { return ST_NOALLOC_SCRATCH_BYTES; }
+
+st_status st_attn3d_fwd_noalloc(const void* q, const void* k, const void* v, int T, int H, int W,
+                                int n_text, int heads, int d, const int rope_split[3], float theta,
+                                st_dtype dtype, void* out, hipStream_t stream) {
+    long long n = 0;
+    st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
+    if (s != ST_OK) return s;
+    if (!theta_ok(theta)) return ST_ERR_UNSUPPORTED;
+    const size_t need = st_attn3d_workspace_bytes(T, H, W, n_text, heads, d, rope_split, dtype);
+    if (need == 0) return ST_ERR_SHAPE;
+    if (need > ST_NOALLOC_SCRATCH_BYTES) return ST_ERR_WORKSPACE;
+    hipError_t e;
+    void* ws = scratch_on_current_device(&e);
+    if (!ws) return hip_fail(e);
+    // The same launches as st_attn3d_fwd with the scratch as its workspace (no byte of it needs to
+    // start at zero: the table and the staged tiles are written whole, every block flag is
+    // rewritten by the attention launch that reads it).
+    return st_attn3d_fwd(q, k, v, T, H, W, n_text, heads, d, rope_split, theta, dtype, ws, need, out,
+                         stream);
 }
 
 st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T, int H, int W,

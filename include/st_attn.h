@@ -143,6 +143,31 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
                               void* workspace, size_t ws_bytes, void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Allocation-free full 3D attention, for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The result is st_attn3d_fwd's, bit for bit (same launches); its workspace is a static device
+ * array of ST_NOALLOC_SCRATCH_BYTES inside the library, of which each GPU holds one copy from the
+ * library's load until the process ends.  The first call on a device takes the array's device
+ * address (hipGetSymbolAddress, with that device current); no call allocates or frees anything.
+ *   Limit   st_attn3d_workspace_bytes(...) for the request must not exceed
+ *           ST_NOALLOC_SCRATCH_BYTES (128 MiB: e.g. 21x30x52 tokens x 12 heads needs 100.7 MB);
+ *           larger requests return ST_ERR_WORKSPACE with nothing enqueued.
+ *   Races   Every call on one GPU uses that GPU's single array: calls whose stream work overlaps
+ *           on one GPU (other streams, other host threads) race and give wrong results.  Calls
+ *           serialised on one stream are safe.
+ * Arguments, layout and errors otherwise as st_attn3d_fwd; a failure to obtain the array's
+ * address returns ST_ERR_HIP.
+ * ------------------------------------------------------------------------------------------- */
+#define ST_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+size_t st_attn3d_noalloc_scratch_bytes(void);
+
+st_status st_attn3d_fwd_noalloc(const void* q, const void* k, const void* v,
+                                int T, int H, int W, int n_text, int heads, int d,
+                                const int rope_split[3], float theta, st_dtype dtype,
+                                void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Factorised attention (first page, self-test answer 2): stage 1 attends inside each frame
  * (T sequences of H*W rows), stage 2 attends along time at each spatial position (H*W sequences
  * of T rows) with the same rotated q and k and stage 1's output as values.  No text rows

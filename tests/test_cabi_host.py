@@ -429,3 +429,30 @@ def test_window_rejects_invalid_arguments(lib):
     assert f(T=64, H=64, W=64, heads=64, window=(4, 4, 4), ws_bytes=1 << 40) == ST_ERR_UNSUPPORTED
     # fp32: at most 65535 windows (one grid row of workgroups per window)
     assert f(T=64, H=64, W=32, dtype=1, d=64, split=(22, 20, 22), window=(1, 1, 1)) == ST_ERR_SHAPE
+
+
+def test_noalloc_rejects_invalid_arguments_before_any_device_call(lib):
+    # Every request below fails validation, so no HIP call (not even the scratch address lookup)
+    # is made: these run without a GPU.
+    def f(**kw):
+        a = dict(q=Q, k=K, v=V, T=3, H=4, W=6, n_text=0, heads=2, d=128, split=(44, 42, 42),
+                 theta=1e4, dtype=0, out=OUT)
+        a.update(kw)
+        return lib.st_attn3d_fwd_noalloc(a["q"], a["k"], a["v"], a["T"], a["H"], a["W"], a["n_text"],
+                                         a["heads"], a["d"], sp(*a["split"]), a["theta"], a["dtype"],
+                                         a["out"], None)
+    cap = lib.st_attn3d_noalloc_scratch_bytes()
+    assert cap == 128 << 20
+    assert f(q=None) == ST_ERR_NULL
+    assert f(out=None) == ST_ERR_NULL
+    assert f(T=0) == ST_ERR_SHAPE
+    assert f(split=(44, 44, 42)) == ST_ERR_SPLIT
+    assert f(d=64, split=(20, 22, 22)) == ST_ERR_UNSUPPORTED
+    assert f(theta=0.0) == ST_ERR_UNSUPPORTED
+    assert f(out=Q) == ST_ERR_ALIAS
+    assert f(q=Q + 8) == ST_ERR_ALIGN
+    # past the scratch: 21 x 45 x 80 tokens x 12 heads needs more than 128 MiB of staged tiles
+    assert lib.st_attn3d_workspace_bytes(21, 45, 80, 0, 12, 128, sp(44, 42, 42), 0) > cap
+    assert f(T=21, H=45, W=80, heads=12) == ST_ERR_WORKSPACE
+    # and the bench workload (21 x 30 x 52 x 12) fits
+    assert lib.st_attn3d_workspace_bytes(21, 30, 52, 0, 12, 128, sp(44, 42, 42), 0) <= cap
