@@ -102,6 +102,148 @@ def cpu_baseline(rows_per_head: int):
     }
 
 
+ALL_LEGS = ["wan13b_17f", "wan14b_720p", "hunyuan_joint", "factorized", "rope_apply", "fused_rope",
+            "cross_512", "merge2", "qkv_rope", "window_7x10x13"]
+
+
+def _timed(fn, stream, reps, warm=2):
+    """Average ms per call of fn() over `reps` back-to-back calls bracketed by HIP events on the
+    launch stream (after `warm` untimed calls)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _mfma_rate(flop, ms):
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOPs": round(tf, 2), "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
+def _full_config(name, grid, heads, n_text, split, seed, row_scale, stream, dev):
+    """Full attention at one of the workload configurations, on its seeded inputs."""
+    import numpy as np
+    import torch
+    import full_spatiotemporal_attention_amd as fa
+    from st_inputs import make_qkv
+    n = grid[0] * grid[1] * grid[2] + n_text
+    t0 = time.perf_counter()
+    x = make_qkv(n, heads, D, seed, "bf16", row_scale=row_scale)
+    qq, kk, vv = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+                  for b in (x.q_bits, x.k_bits, x.v_bits))
+    del x
+    eprint(f"  {name}: inputs generated in {time.perf_counter() - t0:.1f} s")
+    ws = torch.empty(fa.attn3d_workspace_bytes(grid, heads, n_text, D, split), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(qq)
+    ms = _timed(lambda: fa.attn3d(qq, kk, vv, grid, n_text, split, THETA, out=o, workspace=ws), stream,
+                reps=3 if n > 50000 else 10, warm=1 if n > 50000 else 2)
+    r = _mfma_rate(4.0 * n * n * heads * D, ms)
+    r.update({"grid": list(grid), "heads": heads, "n_text": n_text, "rope_split": list(split),
+              "inputs": "N(0,1)" + (" x per-row U(%g,%g)" % row_scale if row_scale else "") +
+                        f" bf16, PCG64 seeds {seed}..{seed + 2}", "scope": "stage + attend (st_attn3d_fwd)"})
+    del qq, kk, vv, ws, o
+    return r
+
+
+def run_legs(legs, q, k, v, out, full_ms, stream, dev):
+    """Timings after the headline: the other workload configurations and the other entry points
+    (factorised path, stand-alone RoPE, fused-RoPE variant, cross-attention, merge, QKV projection,
+    windows).  Each leg can be run alone (--legs), so a profile can cover exactly one leg."""
+    import torch
+    import full_spatiotemporal_attention_amd as fa
+    from full_spatiotemporal_attention_amd import _lib
+    n = GRID[0] * GRID[1] * GRID[2]
+    flop = 4.0 * n * n * HEADS * D
+    extras = {}
+    reps = 10
+    for leg in legs:
+        if leg not in ALL_LEGS:
+            raise SystemExit(f"unknown leg {leg!r}; known: {', '.join(ALL_LEGS)}")
+        eprint(f"leg {leg}")
+        if leg == "wan13b_17f":
+            extras[leg] = _full_config(leg, (5, 30, 52), 12, 0, SPLIT, 1000, None, stream, dev)
+        elif leg == "wan14b_720p":
+            extras[leg] = _full_config(leg, (21, 45, 80), 40, 0, SPLIT, 3000, (0.5, 2.0), stream, dev)
+        elif leg == "hunyuan_joint":
+            extras[leg] = _full_config(leg, (33, 45, 80), 24, 256, (16, 56, 56), 4000, None, stream, dev)
+        elif leg == "factorized":
+            ws = torch.empty(fa.attn_factorized_workspace_bytes(GRID, HEADS, D, SPLIT), dtype=torch.uint8,
+                             device=dev)
+            fout = torch.empty_like(q)
+            ms = _timed(lambda: fa.attn_factorized(q, k, v, GRID, SPLIT, THETA, out=fout, workspace=ws),
+                        stream, reps)
+            fflop = (4.0 * GRID[0] * (GRID[1] * GRID[2]) ** 2 * HEADS * D
+                     + 4.0 * GRID[1] * GRID[2] * GRID[0] ** 2 * HEADS * D)
+            extras[leg] = {"ms": round(ms, 4), "flop": fflop,
+                           "full_over_factorized_time": round(full_ms / ms, 3),
+                           "full_over_factorized_flop": round(flop / fflop, 3)}
+        elif leg == "rope_apply":
+            rws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
+            rout = torch.empty_like(q)
+            ms = _timed(lambda: fa.rope3d_apply(q, GRID, 0, SPLIT, THETA, out=rout, workspace=rws), stream, reps)
+            by = 2.0 * q.numel() * q.element_size()
+            extras[leg] = {"ms": round(ms, 4), "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        elif leg == "fused_rope":
+            fws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
+            fout = torch.empty_like(q)
+            ms = _timed(lambda: fa.attn3d_fused(q, k, v, GRID, 0, SPLIT, THETA, out=fout, workspace=fws),
+                        stream, reps)
+            extras[leg] = _mfma_rate(flop, ms)
+        elif leg == "cross_512":
+            # Text cross-attention next to the self-attention (Wan: at most 512 text tokens).
+            n_txt = 512
+            g = torch.Generator(device=dev).manual_seed(SEED + 20)
+            kt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=g).to(torch.bfloat16)
+            vt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=g).to(torch.bfloat16)
+            cws = torch.empty(max(256, _lib.load().st_attn_cross_workspace_bytes(n, n_txt, HEADS, D, _lib.ST_BF16)),
+                              dtype=torch.uint8, device=dev)
+            cout = torch.empty_like(q)
+            ms = _timed(lambda: fa.attn_cross(q, kt_, vt_, out=cout, workspace=cws), stream, reps)
+            extras[leg] = _mfma_rate(4.0 * n * n_txt * HEADS * D, ms)
+        elif leg == "merge2":
+            # Merge of two partial results over the whole grid (HBM-bound: 2 reads + 1 write of O).
+            lse_a = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
+            lse_b = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
+            other = torch.empty_like(q).copy_(out)
+            mo, ml = torch.empty_like(q), torch.empty_like(lse_a)
+            ms = _timed(lambda: fa.attn_merge([(out, lse_a), (other, lse_b)], out=mo, lse_out=ml), stream, reps)
+            by = 3.0 * q.numel() * 2 + 3.0 * n * HEADS * 4
+            extras[leg] = {"ms": round(ms, 4), "GBps": round(by / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        elif leg == "qkv_rope":
+            # QKV projection with the rotation of q and k in its epilogue (Wan2.1-1.3B: C = 1536).
+            C = HEADS * D
+            gx = torch.Generator(device=dev).manual_seed(SEED + 30)
+            xq = torch.randn(n, C, device=dev, generator=gx).to(torch.bfloat16)
+            wq = (torch.randn(3 * C, C, device=dev, generator=gx) / C ** 0.5).to(torch.bfloat16)
+            bq = (0.1 * torch.randn(3 * C, device=dev, generator=gx)).to(torch.bfloat16)
+            qws = torch.empty(max(256, fa.rope3d_table_bytes(GRID, SPLIT)), dtype=torch.uint8, device=dev)
+            ms = _timed(lambda: fa.qkv_rope(xq, wq, GRID, bias=bq, rope_split=SPLIT, workspace=qws), stream, reps)
+            extras[leg] = _mfma_rate(2.0 * n * C * 3 * C, ms)
+            del xq, wq, bq
+        elif leg == "window_7x10x13":
+            # Local 3D windows of 7 x 10 x 13 = 910 tokens (36 windows over the grid).
+            WIN = (7, 10, 13)
+            L_win = WIN[0] * WIN[1] * WIN[2]
+            wws = torch.empty(max(256, _lib.load().st_attn3d_window_workspace_bytes(
+                *GRID, HEADS, D, _lib.split_arg(SPLIT), _lib.split_arg(WIN), _lib.ST_BF16)), dtype=torch.uint8,
+                device=dev)
+            wout = torch.empty_like(q)
+            ms = _timed(lambda: fa.attn_window(q, k, v, GRID, WIN, SPLIT, THETA, out=wout, workspace=wws),
+                        stream, reps)
+            extras[leg] = _mfma_rate(4.0 * n * L_win * HEADS * D, ms)
+        torch.cuda.synchronize()
+        eprint(f"  {leg}: {extras[leg]}")
+    return extras
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +251,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip factorised and RoPE timings")
+    ap.add_argument("--no-extras", action="store_true", help="skip every leg after the headline")
+    ap.add_argument("--legs", default=",".join(ALL_LEGS),
+                    help="comma-separated legs timed after the headline (default: all): " + ", ".join(ALL_LEGS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one 256 MiB device-to-device copy first (scale for HBM counters)")
     args = ap.parse_args()
@@ -225,145 +369,10 @@ def main():
     }
 
     if not args.no_extras:
-        extras = {}
-        ws = torch.empty(fa.attn_factorized_workspace_bytes(GRID, HEADS, D, SPLIT), dtype=torch.uint8,
-                         device=dev)
-        fout = torch.empty_like(q)
-        for _ in range(2):
-            fa.attn_factorized(q, k, v, GRID, SPLIT, THETA, out=fout, workspace=ws)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        e0.record(stream)
-        for _ in range(reps):
-            fa.attn_factorized(q, k, v, GRID, SPLIT, THETA, out=fout, workspace=ws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fact_ms = e0.elapsed_time(e1) / reps
-        extras["factorized_ms"] = round(fact_ms, 4)
-        extras["full_over_factorized_time"] = round(ev_ms / fact_ms, 3)
-        extras["full_over_factorized_flop"] = round(
-            flop / (4.0 * GRID[0] * (GRID[1] * GRID[2]) ** 2 * HEADS * D
-                    + 4.0 * GRID[1] * GRID[2] * GRID[0] ** 2 * HEADS * D), 3)
-        rws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
-        rout = torch.empty_like(q)
-        for _ in range(2):
-            fa.rope3d_apply(q, GRID, 0, SPLIT, THETA, out=rout, workspace=rws)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.rope3d_apply(q, GRID, 0, SPLIT, THETA, out=rout, workspace=rws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        rope_ms = e0.elapsed_time(e1) / reps
-        rope_bytes = 2.0 * q.numel() * q.element_size()
-        extras["rope_apply_ms"] = round(rope_ms, 4)
-        extras["rope_apply_GBps"] = round(rope_bytes / (rope_ms * 1e-3) / 1e9, 1)
-        extras["rope_apply_hbm_frac"] = round(rope_bytes / (rope_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-        # A/B: RoPE of K fused into every tile load (no staging pass), same numerics.
-        fws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            fa.attn3d_fused(q, k, v, GRID, 0, SPLIT, THETA, out=fout, workspace=fws)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.attn3d_fused(q, k, v, GRID, 0, SPLIT, THETA, out=fout, workspace=fws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        fused_ms = e0.elapsed_time(e1) / reps
-        extras["fused_rope_step_ms"] = round(fused_ms, 4)
-        extras["fused_rope_TFLOPs"] = round(flop / (fused_ms * 1e-3) / 1e12, 2)
-        # Text cross-attention next to the self-attention (Wan: at most 512 text tokens).
-        n_txt = 512
-        kt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=torch.Generator(device=dev).manual_seed(SEED + 20)).to(torch.bfloat16)
-        vt_ = torch.randn(n_txt, HEADS, D, device=dev, generator=torch.Generator(device=dev).manual_seed(SEED + 21)).to(torch.bfloat16)
-        cws = torch.empty(max(256, fa._lib.load().st_attn_cross_workspace_bytes(n, n_txt, HEADS, D, _lib.ST_BF16)),
-                          dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            fa.attn_cross(q, kt_, vt_, out=fout, workspace=cws)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.attn_cross(q, kt_, vt_, out=fout, workspace=cws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cross_ms = e0.elapsed_time(e1) / reps
-        cross_flop = 4.0 * n * n_txt * HEADS * D
-        extras["cross_512_ms"] = round(cross_ms, 4)
-        extras["cross_512_TFLOPs"] = round(cross_flop / (cross_ms * 1e-3) / 1e12, 2)
-        # Merge of two partial results over the whole grid (HBM-bound: 2 reads + 1 write of O).
-        lse_a = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
-        lse_b = torch.zeros(n, HEADS, dtype=torch.float32, device=dev)
-        mo = torch.empty_like(q)
-        ml = torch.empty_like(lse_a)
-        for _ in range(2):
-            fa.attn_merge([(out, lse_a), (fout, lse_b)], out=mo, lse_out=ml)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.attn_merge([(out, lse_a), (fout, lse_b)], out=mo, lse_out=ml)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        merge_ms = e0.elapsed_time(e1) / reps
-        merge_bytes = 3.0 * q.numel() * 2 + 3.0 * n * HEADS * 4
-        extras["merge2_ms"] = round(merge_ms, 4)
-        extras["merge2_GBps"] = round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1)
-        # QKV projection with the rotation of q and k in its epilogue (Wan2.1-1.3B: C = 1536).
-        C = HEADS * D
-        gx = torch.Generator(device=dev).manual_seed(SEED + 30)
-        xq = torch.randn(n, C, device=dev, generator=gx).to(torch.bfloat16)
-        wq = (torch.randn(3 * C, C, device=dev, generator=gx) / C ** 0.5).to(torch.bfloat16)
-        bq = (0.1 * torch.randn(3 * C, device=dev, generator=gx)).to(torch.bfloat16)
-        qws = torch.empty(max(256, fa.rope3d_table_bytes(GRID, SPLIT)), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            fa.qkv_rope(xq, wq, GRID, bias=bq, rope_split=SPLIT, workspace=qws)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.qkv_rope(xq, wq, GRID, bias=bq, rope_split=SPLIT, workspace=qws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        qkv_ms = e0.elapsed_time(e1) / reps
-        extras["qkv_rope_ms"] = round(qkv_ms, 4)
-        extras["qkv_rope_TFLOPs"] = round(2.0 * n * C * 3 * C / (qkv_ms * 1e-3) / 1e12, 2)
-        del xq, wq, bq
-        # Local 3D windows of 7 x 10 x 13 = 910 tokens (36 windows over the grid).
-        WIN = (7, 10, 13)
-        L_win = WIN[0] * WIN[1] * WIN[2]
-        wws = torch.empty(max(256, fa._lib.load().st_attn3d_window_workspace_bytes(
-            *GRID, HEADS, D, _lib.split_arg(SPLIT), _lib.split_arg(WIN), _lib.ST_BF16)), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            fa.attn_window(q, k, v, GRID, WIN, SPLIT, THETA, out=fout, workspace=wws)
-        e0.record(stream)
-        for _ in range(reps):
-            fa.attn_window(q, k, v, GRID, WIN, SPLIT, THETA, out=fout, workspace=wws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        win_ms = e0.elapsed_time(e1) / reps
-        extras["window_7x10x13_ms"] = round(win_ms, 4)
-        extras["window_7x10x13_TFLOPs"] = round(4.0 * n * L_win * HEADS * D / (win_ms * 1e-3) / 1e12, 2)
-        # The two long configurations at full size, timed the same way as the headline (they are
-        # parity cases on sampled rows elsewhere): the Wan-14B-shaped 720p clip (21 x 45 x 80,
-        # 40 heads) and HunyuanVideo's joint sequence (33 x 45 x 80 video rows + 256 appended text
-        # rows, 24 heads, split 16/56/56).  Synthetic N(0,1) bf16 inputs.
-        del fout, ws, rout, rws, fws, wws
-        for name, grid_l, heads_l, n_text_l, split_l in (("wan14b_720p", (21, 45, 80), 40, 0, SPLIT),
-                                                        ("hunyuan_joint", (33, 45, 80), 24, 256, (16, 56, 56))):
-            n_l = grid_l[0] * grid_l[1] * grid_l[2] + n_text_l
-            gl = torch.Generator(device=dev).manual_seed(SEED + 40)
-            ql, kl, vl = (torch.randn(n_l, heads_l, D, device=dev, generator=gl).to(torch.bfloat16)
-                          for _ in range(3))
-            wsl = torch.empty(fa.attn3d_workspace_bytes(grid_l, heads_l, n_text_l, D, split_l),
-                              dtype=torch.uint8, device=dev)
-            outl = torch.empty_like(ql)
-            fa.attn3d(ql, kl, vl, grid_l, n_text_l, split_l, THETA, out=outl, workspace=wsl)
-            reps_l = 3
-            e0.record(stream)
-            for _ in range(reps_l):
-                fa.attn3d(ql, kl, vl, grid_l, n_text_l, split_l, THETA, out=outl, workspace=wsl)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms_l = e0.elapsed_time(e1) / reps_l
-            flop_l = 4.0 * n_l * n_l * heads_l * D
-            extras[f"{name}_ms"] = round(ms_l, 3)
-            extras[f"{name}_TFLOPs"] = round(flop_l / (ms_l * 1e-3) / 1e12, 2)
-            del ql, kl, vl, wsl, outl
+        legs = [l for l in args.legs.split(",") if l]
+        extras = run_legs(legs, q, k, v, out, ev_ms, stream, dev)
         result["extras"] = extras
-        eprint(f"extras: {extras}")
+        eprint(f"extras: {json.dumps(extras)}")
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_rows)
