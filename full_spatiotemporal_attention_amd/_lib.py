@@ -67,11 +67,16 @@ class StError(RuntimeError):
 _LIB = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libstattn.so once; raise if it has not been built (there is no fallback path)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libstattn.so once; raise if it has not been built (there is no fallback path).
+
+    ``STATTN_LIB`` in the environment names another build of the same library (the sanitized
+    debug build of build_sanitized.py); by default the in-tree libstattn.so is loaded."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    if path is None:
+        path = os.environ.get("STATTN_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(
             f"{path} is missing: build it with `python -m full_spatiotemporal_attention_amd.build` "

@@ -4,6 +4,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -97,6 +98,14 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 size_t elem_size(st_dtype dt) { return dt == ST_BF16 ? 2 : 4; }
 
 bool theta_ok(float theta) { return isfinite(theta) && theta > 0.0f; }
+
+// A C caller may pass any int as st_dtype; in C++ loading an enum value outside its enumerators'
+// range is undefined, so the entry points check the code through its bytes before using it.
+bool dtype_known(const st_dtype& dt) {
+    int code;
+    memcpy(&code, &dt, sizeof code);
+    return code == ST_BF16 || code == ST_F32;
+}
 
 // Checks shared by the attention entry points (tensor pointers, shapes, dtype, split, aliasing).
 st_status check_attn(const void* q, const void* k, const void* v, const void* out, int T, int H,
@@ -252,6 +261,7 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
 
 size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
                                  const int rope_split[3], st_dtype dtype) {
+    if (!dtype_known(dtype)) return 0;
     long long n = 0;
     if (!rope_split || !grid_ok(T, H, W, n_text, &n) || heads < 1) return 0;
     if (check_split(rope_split, d) != ST_OK) return 0;
@@ -267,6 +277,7 @@ size_t st_attn3d_fused_workspace_bytes(int T, int H, int W, const int rope_split
 st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int heads, int d,
                           const int rope_split[3], float theta, st_dtype dtype, void* workspace,
                           size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     // Only k is read by this step; it stands in for q and v in the shared checks.
     st_status s = check_attn(k, k, k, workspace, T, H, W, n_text, heads, d, rope_split, dtype, &n);
@@ -292,6 +303,7 @@ st_status st_attn3d_stage(const void* k, int T, int H, int W, int n_text, int he
 st_status st_attn3d_attend(const void* q, const void* v, int T, int H, int W, int n_text, int heads,
                            int d, const int rope_split[3], st_dtype dtype, void* workspace,
                            size_t ws_bytes, void* out, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     if (!workspace) return ST_ERR_NULL;
     st_status s = check_attn(q, q, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
@@ -315,6 +327,7 @@ st_status st_attn3d_fwd(const void* q, const void* k, const void* v, int T, int 
                         int n_text, int heads, int d, const int rope_split[3], float theta,
                         st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
                         hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
@@ -346,6 +359,7 @@ size_t st_attn3d_noalloc_scratch_bytes(void) { return ST_NOALLOC_SCRATCH_BYTES; 
 st_status st_attn3d_fwd_noalloc(const void* q, const void* k, const void* v, int T, int H, int W,
                                 int n_text, int heads, int d, const int rope_split[3], float theta,
                                 st_dtype dtype, void* out, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
@@ -367,6 +381,7 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T
                               int n_text, int heads, int d, const int rope_split[3], float theta,
                               st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
                               hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     st_status s = check_attn(q, k, v, out, T, H, W, n_text, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
@@ -392,6 +407,7 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T
 
 size_t st_attn_factorized_workspace_bytes(int T, int H, int W, int heads, int d,
                                           const int rope_split[3], st_dtype dtype) {
+    if (!dtype_known(dtype)) return 0;
     if (!rope_split || heads < 1 || d < 2 || (d & 1)) return 0;
     long long n = 0;
     if (!grid_ok(T, H, W, 0, &n)) return 0;
@@ -406,6 +422,7 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
                                  int heads, int d, const int rope_split[3], float theta,
                                  st_dtype dtype, void* workspace, size_t ws_bytes, void* out,
                                  hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     st_status s = check_attn(q, k, v, out, T, H, W, 0, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
@@ -455,6 +472,7 @@ st_status st_attn_factorized_fwd(const void* q, const void* k, const void* v, in
 size_t st_attn3d_window_workspace_bytes(int T, int H, int W, int heads, int d,
                                         const int rope_split[3], const int window[3],
                                         st_dtype dtype) {
+    if (!dtype_known(dtype)) return 0;
     long long n = 0;
     if (!rope_split || !window || heads < 1 || !grid_ok(T, H, W, 0, &n)) return 0;
     if (check_split(rope_split, d) != ST_OK) return 0;
@@ -471,6 +489,7 @@ st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int 
                                int heads, int d, const int rope_split[3], float theta,
                                const int window[3], st_dtype dtype, void* workspace,
                                size_t ws_bytes, void* out, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     long long n = 0;
     st_status s = check_attn(q, k, v, out, T, H, W, 0, heads, d, rope_split, dtype, &n);
     if (s != ST_OK) return s;
@@ -517,6 +536,7 @@ st_status st_attn3d_window_fwd(const void* q, const void* k, const void* v, int 
 st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_text, int heads,
                           int d, const int rope_split[3], float theta, st_dtype dtype,
                           void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     if (!x || !y || !rope_split || !workspace) return ST_ERR_NULL;
     long long n = 0;
     if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
@@ -552,6 +572,7 @@ st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_tex
 // ---- text cross-attention --------------------------------------------------------------------
 
 size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dtype dtype) {
+    if (!dtype_known(dtype)) return 0;
     if (n_q < 1 || n_kv < 1 || n_q >= kMaxRows || n_kv >= kMaxRows || heads < 1 || heads > 65535)
         return 0;
     if (d < 2 || (d & 1)) return 0;
@@ -564,6 +585,7 @@ size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dty
 st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,
                             int heads, int d, st_dtype dtype, void* workspace, size_t ws_bytes,
                             void* out, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     if (!q || !k || !v || !out || !workspace) return ST_ERR_NULL;
     if (n_q < 1 || n_kv < 1 || n_q >= kMaxRows || n_kv >= kMaxRows) return ST_ERR_SHAPE;
     if (heads < 1 || heads > 65535 || d < 2 || (d & 1)) return ST_ERR_SHAPE;
@@ -624,6 +646,7 @@ st_status st_qkv_rope_fwd(const void* x, const void* w, const void* bias, int T,
                           int n_text, int heads, int d, const int rope_split[3], float theta,
                           st_dtype dtype, void* workspace, size_t ws_bytes, void* q, void* k,
                           void* v, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     if (!x || !w || !q || !k || !v || !workspace || !rope_split) return ST_ERR_NULL;
     long long n = 0;
     if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
@@ -679,6 +702,7 @@ st_status st_qkv_rope_fwd(const void* x, const void* w, const void* bias, int T,
 
 size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
                                          const int rope_split[3], st_dtype dtype, int kv_count) {
+    if (!dtype_known(dtype)) return 0;
     long long n = 0;
     if (!rope_split || !grid_ok(T, H, W, n_text, &n) || heads < 1 || heads > 65535) return 0;
     if (check_split(rope_split, d) != ST_OK) return 0;
@@ -694,6 +718,7 @@ st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int
                                 st_dtype dtype, int q_begin, int q_count, int kv_begin,
                                 int kv_count, void* workspace, size_t ws_bytes, void* out,
                                 float* lse, hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     if (!q || !k || !v || !out || !lse || !workspace || !rope_split) return ST_ERR_NULL;
     long long n = 0;
     if (!grid_ok(T, H, W, n_text, &n)) return ST_ERR_SHAPE;
@@ -756,6 +781,7 @@ st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int
 st_status st_attn_merge(int n_parts, const void* const* o_parts, const float* const* lse_parts,
                         int n_rows, int heads, int d, st_dtype dtype, void* out, float* lse_out,
                         hipStream_t stream) {
+    if (!dtype_known(dtype)) return ST_ERR_UNSUPPORTED;
     if (!o_parts || !lse_parts || !out) return ST_ERR_NULL;
     if (n_parts < 1 || n_parts > st::kMaxMergeParts) return ST_ERR_SHAPE;
     if (n_rows < 1 || n_rows >= kMaxRows || heads < 1 || heads > 65535) return ST_ERR_SHAPE;
@@ -792,7 +818,11 @@ st_status st_attn_merge(int n_parts, const void* const* o_parts, const float* co
 }
 
 const char* st_status_str(st_status s) {
-    switch (s) {
+    // A C caller may pass any int; in C++ loading an st_status outside the enumerators' range is
+    // undefined, so the code is read through its bytes.
+    int code;
+    memcpy(&code, &s, sizeof code);
+    switch (code) {
         case ST_OK: return "ok";
         case ST_ERR_NULL: return "null pointer";
         case ST_ERR_SHAPE: return "shape out of range";
