@@ -68,6 +68,7 @@ constexpr int PREF = 3;                          // step j fetches tile j + PREF
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
 constexpr int WIN_TABLE = 8192;                  // window mode: V row offsets kept in LDS (32 KB)
+constexpr int LDS_TABLE = WIN_TABLE / 2;          // fast launch: rotation table entries kept in LDS
 constexpr float OVF_SUM = 0x1p64f;   // fast launch: a row sum this large (or not finite) flags the item
 constexpr float LAZY_LOG2 = 8.0f;  // move the offset when a row max exceeds it by more than this
 
@@ -657,8 +658,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 template <bool WIN>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
-    __shared__ uint32_t win_vrow[WIN ? WIN_TABLE : 1];   // window mode: byte offset of each V row
+    // 32 KB beside the tiles: in window mode the byte offset of each V row of the window; otherwise
+    // the rotation table, copied once per workgroup when it has at most LDS_TABLE entries.
+    __shared__ __attribute__((aligned(16))) uint32_t lds_aux[WIN_TABLE];
+    uint32_t* const win_vrow = lds_aux;
+    const float2* const tab_lds = reinterpret_cast<const float2*>(lds_aux);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
+
+    // The Q rotation of every item gathers 32 table entries per lane.  From global memory these
+    // gathers are most of the prologue's vector-memory instructions, which all CUs issue at the
+    // same time; from LDS they cost a few cycles each.
+    const bool table_in_lds = !WIN && p.g.identity < LDS_TABLE;
+    if (table_in_lds) {
+        float2* const t = reinterpret_cast<float2*>(lds_aux);
+        for (int i = threadIdx.x; i <= p.g.identity; i += NTHREADS) t[i] = p.table[i];
+        __syncthreads();
+    }
 
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
     // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
@@ -782,6 +797,35 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) raw[qb][ks] = ld16(qp + 32 * ks);
             }
+            // All 32 table entries are loaded before any is used: the empty asm (a memory clobber)
+            // keeps the loads above it, so they are in flight together.  Left to itself the
+            // compiler placed each load just before its use, behind a wait for everything issued
+            // before it: 32 round trips per item.
+            float2 cs[2][4][4];
+            if (table_in_lds) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int p0 = 16 * ks + i;
+                            const int base = p0 >= g2 ? bw[qb] : (p0 >= g1 ? bh[qb] : bt[qb]);
+                            cs[qb][ks][i] = tab_lds[base + p0];
+                        }
+            } else {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int p0 = 16 * ks + i;
+                            const int base = p0 >= g2 ? bw[qb] : (p0 >= g1 ? bh[qb] : bt[qb]);
+                            cs[qb][ks][i] = p.table[base + p0];
+                        }
+            }
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -790,11 +834,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                     uint32_t o[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int p0 = 16 * ks + i;
-                        const int base = p0 >= g2 ? bw[qb] : (p0 >= g1 ? bh[qb] : bt[qb]);
-                        const float2 cs = p.table[base + p0];
                         float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
-                        rotate_pair(x0, x1, cs);
+                        rotate_pair(x0, x1, cs[qb][ks][i]);
                         o[i] = pack_f16x2(x0 * sc, x1 * sc);
                     }
                     qreg[qb][ks] = __builtin_bit_cast(f16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
@@ -1042,20 +1083,69 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
         }
 
         // ---- epilogue: O / l -> bf16 ---------------------------------------------------------------
+        // Lane (l16, lg) holds 4 channels of its row per channel block db.  Two lane swaps per pair
+        // of blocks (2 d, 2 d + 1) give it 8 consecutive channels, 32 d + 8 lg .. +7.  Neighbouring
+        // lanes l16 = 2 m, 2 m + 1 then trade one such piece, so that a store covers whole
+        // 128-byte lines: 8 rows x 128 bytes per store, where storing the blocks as they are writes
+        // 32 bytes into each of 16 rows (about half of the time between two items went there).
+        // The lane's parity is formed here from the lane count (mbcnt), not kept from before the
+        // loop: one more value live through the tile loop leaves its schedule too few registers
+        // to read the K operands ahead.
+        const bool odd = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) & 1u) != 0;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const float l_tot = xquad_sum(l_run[qb]);
             const float inv = 1.0f / l_tot;
             if (p.lse && q_valid[qb] && lg == 0)
                 p.lse[(long long)q_row[qb] * p.heads + head] = m_run[qb] * 0.6931471805599453f + __logf(l_tot);
-            if (q_valid[qb]) {
-                uint16_t* op = p.out + q_row[qb] * row_stride + (long long)head * D + 4 * lg;
+            uint32_t w[4][4];
 #pragma unroll
-                for (int db = 0; db < 8; ++db) {
-                    uint2 u;
-                    u.x = pack_bf16x2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv);
-                    u.y = pack_bf16x2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
-                    *reinterpret_cast<uint2*>(op + 16 * db) = u;
+            for (int d = 0; d < 4; ++d) {
+                // A: block 2 d (channels 32 d + 4 lg ..), B: block 2 d + 1 (32 d + 16 + 4 lg ..).
+                const uint32_t a0 = pack_bf16x2(oacc[2 * d][qb][0] * inv, oacc[2 * d][qb][1] * inv);
+                const uint32_t a1 = pack_bf16x2(oacc[2 * d][qb][2] * inv, oacc[2 * d][qb][3] * inv);
+                const uint32_t b0 = pack_bf16x2(oacc[2 * d + 1][qb][0] * inv, oacc[2 * d + 1][qb][1] * inv);
+                const uint32_t b1 = pack_bf16x2(oacc[2 * d + 1][qb][2] * inv, oacc[2 * d + 1][qb][3] * inv);
+                // Upper half (lg 2, 3) of A <-> lower half (lg 0, 1) of B: lanes lg 0, 1 then hold
+                // A of lg and of lg + 2, lanes lg 2, 3 hold B of lg - 2 and of lg.
+                const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+                // Odd 16-lane groups of the first <-> even groups of the second: lane lg then holds
+                // channels 32 d + 8 lg .. +7.
+                const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+                const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+                w[d][0] = t0[0];
+                w[d][1] = t1[0];
+                w[d][2] = t0[1];
+                w[d][3] = t1[1];
+            }
+            // The neighbour's row and whether it lies in the sequence (DPP quad_perm [1, 0, 3, 2]).
+            const int nb_row = __builtin_amdgcn_update_dpp(0, q_row[qb], 0xB1, 0xF, 0xF, false);
+            const int nb_valid = __builtin_amdgcn_update_dpp(0, q_valid[qb] ? 1 : 0, 0xB1, 0xF, 0xF, false);
+            // Store A writes row 2 m, store B row 2 m + 1; the even lane of a pair writes bytes
+            // 128 c + 16 lg .., the odd lane 128 c + 64 + 16 lg .. of that row.
+            const int row_a = odd ? nb_row : q_row[qb];
+            const int row_b = odd ? q_row[qb] : nb_row;
+            const bool ok_a = odd ? nb_valid != 0 : q_valid[qb];
+            const bool ok_b = odd ? q_valid[qb] : nb_valid != 0;
+            const uint16_t* const hb = p.out + (long long)head * D + 8 * lg + (odd ? 32 : 0);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                uint32_t sent[4], got[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    sent[k] = odd ? w[2 * c][k] : w[2 * c + 1][k];
+                    got[k] = __builtin_amdgcn_update_dpp(0u, sent[k], 0xB1, 0xF, 0xF, false);
+                }
+                if (ok_a) {
+                    const uint32_t* v = odd ? got : w[2 * c];
+                    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(hb) + row_a * row_stride + 64 * c) =
+                        make_uint4(v[0], v[1], v[2], v[3]);
+                }
+                if (ok_b) {
+                    const uint32_t* v = odd ? w[2 * c + 1] : got;
+                    *reinterpret_cast<uint4*>(const_cast<uint16_t*>(hb) + row_b * row_stride + 64 * c) =
+                        make_uint4(v[0], v[1], v[2], v[3]);
                 }
             }
         }
