@@ -65,6 +65,8 @@ constexpr int NTHREADS = 512;   // 8 waves
 constexpr int TILE_BYTES = BN * D * 2;           // 16 KB, one K~ or V tile
 constexpr int NBUF = 4;                          // tile j lives in K and V slot j % NBUF
 constexpr int PREF = 3;                          // step j fetches tile j + PREF
+constexpr int KAHEAD = 6;                        // fast kernel: K~ operands read ahead of their MFMAs
+constexpr int VAHEAD = 4;                        // fast kernel: V operands read ahead
 constexpr int V_LDS_BASE = NBUF * TILE_BYTES;    // K slots first, then V slots
 constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES; // 128 KB
 constexpr int WIN_TABLE = 8192;                  // window mode: V row offsets kept in LDS (32 KB)
@@ -905,6 +907,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
             return xquad_max(mx);
         };
 
+
         // Output O^T block (db, qb): lane (l16, lg) holds channels 16 db + 4 lg + i of query
         // 16 qb + l16.
         f32x4_t oacc[8][2];
@@ -969,82 +972,92 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
                 }
             }
 
-            // Scores of tile j+1 (MFMA) while the weights of tile j are formed (VALU).  After the
-            // last tile the K slot holds stale data and these scores are discarded.
-            // B operand of PV chunk kk (keys 32 kk ..) for query block qb: blocks 2 kk and 2 kk + 1.
-            // The rounded weights are summed in two chains, one of them the running row sum.
-            bf16x8_t pb[2][2];
+            // The step in a fixed order, fenced (sched_barrier) in groups of two MFMAs: one K~ or V
+            // operand for both query blocks.  The fences keep the schedule of this loop from
+            // depending on code elsewhere in the kernel (left to the scheduler, the K~ reads moved
+            // next to their MFMAs whenever other code changed the register estimate), and cost
+            // nothing against the scheduler's best order.
+            // Scores of tile j+1 first: operand t = (ks, kb) = (t / 4, t % 4), K~ read KAHEAD
+            // operands ahead.  After the last tile the K slot holds stale data and these scores
+            // are discarded.  Into those 16 groups and the first 8 PV groups (chunk 0, which does
+            // not need chunk 1's weights) go the 16 softmax pairs of tile j, pair i (chunk
+            // kk = i / 8, query block (i / 4) % 2, element pair i % 4) in group 3 i / 2: two
+            // exponentials and one bf16 pack each.  The 16 row-sum dot products take the last 8
+            // groups; the weights are summed in two chains, one of them the running row sum.
+            uint32_t pu[2][2][4];
+            auto do_pair = [&](int i) {
+                const int kk = i >> 3, qb = (i >> 2) & 1, e = i & 3;
+                const int kb = 2 * kk + (e >> 1), i0 = 2 * (e & 1);
+                const float p0 = __builtin_amdgcn_exp2f(sc[kb][qb][i0]);
+                const float p1 = __builtin_amdgcn_exp2f(sc[kb][qb][i0 + 1]);
+                pu[kk][qb][e] = pack_bf16x2(p0, p1);
+            };
+            auto pairs_in = [&](int grp) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if ((3 * i) / 2 == grp) do_pair(i);
+            };
             float l2[2] = {0.0f, 0.0f};
+            auto dots_in = [&](int grp) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    uint32_t u[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int kb = 2 * kk + (e >> 1), i0 = 2 * (e & 1);
-                        const float p0 = __builtin_amdgcn_exp2f(sc[kb][qb][i0]);
-                        const float p1 = __builtin_amdgcn_exp2f(sc[kb][qb][i0 + 1]);
-                        u[e] = pack_bf16x2(p0, p1);
+                for (int i = 0; i < 16; ++i)
+                    if (24 + (i >> 1) == grp) {
+                        const int kk = i >> 3, qb = (i >> 2) & 1, e = i & 3;
                         if (kk)
-                            l2[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                            l2[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu[kk][qb][e]),
                                                                      __builtin_bit_cast(bf16x2_t, one2), l2[qb], false);
                         else
-                            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, u[e]),
+                            l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu[kk][qb][e]),
                                                                         __builtin_bit_cast(bf16x2_t, one2), l_run[qb], false);
                     }
-                    pb[kk][qb] = __builtin_bit_cast(bf16x8_t, make_uint4(u[0], u[1], u[2], u[3]));
-                }
-            l_run[0] += l2[0];
-            l_run[1] += l2[1];
+            };
+            f16x8_t ka[16];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
+            for (int t = 0; t < KAHEAD; ++t) ka[t] = k_operand(b1 * TILE_BYTES, t & 3, t >> 2);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    const f16x8_t ka = k_operand(b1 * TILE_BYTES, kb, ks);
+            for (int t = 0; t < 16; ++t) {
+                if (t + KAHEAD < 16) ka[t + KAHEAD] = k_operand(b1 * TILE_BYTES, (t + KAHEAD) & 3, (t + KAHEAD) >> 2);
+                const int ks = t >> 2, kb = t & 3;
 #pragma unroll
-                    for (int qb = 0; qb < 2; ++qb)
-                        sn[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qreg[qb][ks],
-                                                                            ks == 0 ? negm[qb] : sn[kb][qb], 0, 0, 0);
-                }
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 4, 0);
-#pragma unroll
-            for (int t = 0; t < 12; ++t) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
-            }
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_VALU, 2, 0);
+                for (int qb = 0; qb < 2; ++qb)
+                    sn[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[t], qreg[qb][ks],
+                                                                        ks == 0 ? negm[qb] : sn[kb][qb], 0, 0, 0);
+                pairs_in(t);
+                __builtin_amdgcn_sched_barrier(0);
             }
 
             // Fetch tile j+PREF into the slot read last before the previous barrier.  Past the last
             // tile the fetch repeats the last tile into that free slot (nothing reads it again);
             // issuing unconditionally keeps the count of copies in flight fixed.
             issue_tile(min(j + PREF, ntiles - 1), bp);
+            __builtin_amdgcn_sched_barrier(0);
 
-            // PV of tile j.
+            // PV of tile j: operand t = (kk, db) = (t / 8, t % 8), V read VAHEAD operands ahead.
+            bf16x8_t va[16];
+            bf16x8_t pb[2][2];
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int t = 0; t < VAHEAD; ++t) va[t] = v_operand(b * TILE_BYTES, t & 7, t >> 3);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int db = 0; db < 8; ++db) {
-                    const bf16x8_t va = v_operand(b * TILE_BYTES, db, kk);
+            for (int t = 0; t < 16; ++t) {
+                if (t + VAHEAD < 16) va[t + VAHEAD] = v_operand(b * TILE_BYTES, (t + VAHEAD) & 7, (t + VAHEAD) >> 3);
+                const int kk = t >> 3, db = t & 7;
+                if (t == 0 || t == 8) {
 #pragma unroll
                     for (int qb = 0; qb < 2; ++qb)
-                        oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[kk][qb], oacc[db][qb], 0, 0, 0);
+                        pb[kk][qb] = __builtin_bit_cast(bf16x8_t, make_uint4(pu[kk][qb][0], pu[kk][qb][1],
+                                                                             pu[kk][qb][2], pu[kk][qb][3]));
                 }
-            // Eight transposed reads (four V operands, eight MFMAs) ahead of their use.
-            __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 8, 0);
 #pragma unroll
-            for (int t = 0; t < 24; ++t) {
-                __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+                for (int qb = 0; qb < 2; ++qb)
+                    oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[t], pb[kk][qb], oacc[db][qb], 0, 0, 0);
+                pairs_in(16 + t);
+                dots_in(16 + t);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 8, 0);
+            l_run[0] += l2[0];
+            l_run[1] += l2[1];
 
             // Tile j+2 must have landed before the barrier; tile j+3 (fetched above) may not.
             asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");

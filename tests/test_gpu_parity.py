@@ -263,6 +263,45 @@ def test_fast_launch_redoes_blocks_whose_weights_grow(q_mult, k_ramp):
     assert r2 <= 5e-3 and m2 <= 5e-2
 
 
+# 16,384 video rows and 24 text rows: the last 256-row query tile of the fast launch holds 24 rows
+# (the text rows), so one of its eight waves has rows and the other seven only copy tiles.
+TAIL_TEXT = 24
+
+
+@pytest.mark.parametrize("q_mult,k_ramp", [(1.0, 0.0), (6.0, 3.0)])
+def test_fast_launch_short_last_tile(q_mult, k_ramp):
+    """Every row of the short tile and a sample of the others against the oracle, and all rows
+    against the running-max kernel alone; two runs give the same bits.  With growing key norms the
+    row sums pass 2^64, the flagged blocks go to the guard, and the result still meets the bar."""
+    n = 8 * 32 * 64 + TAIL_TEXT
+    log(f"  short last query tile grid={FAST_GRID} n_text={TAIL_TEXT} heads=2 q_mult={q_mult} k_ramp={k_ramp}")
+    x = make_qkv(n, 2, 128, 333, "bf16", q_mult=q_mult, k_ramp=k_ramp)
+    q, k, v = to_device(x)
+    fast = fa.attn3d(q, k, v, FAST_GRID, n_text=TAIL_TEXT)
+    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0, n_text=TAIL_TEXT)
+    again = fa.attn3d(q, k, v, FAST_GRID, n_text=TAIL_TEXT)
+    torch.cuda.synchronize()
+    assert torch.equal(fast.view(torch.int16), again.view(torch.int16))
+    got, got_safe = host_f64(fast), host_f64(safe)
+    assert np.isfinite(got).all()
+    tail = np.arange(n - TAIL_TEXT, n)
+    rows = np.union1d(sample_rows(n, n - TAIL_TEXT, 2048, 128, 333), tail)
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, FAST_GRID, TAIL_TEXT, WAN, 10000.0, rows=rows, heads=[0, 1])
+    m_t, r_t = errors(got[tail], oracle.full_attention_ref(x.q, x.k, x.v, FAST_GRID, TAIL_TEXT, WAN, 10000.0,
+                                                           rows=tail, heads=[0, 1]))
+    log(f"    short tile vs oracle: max_abs={m_t:.3e} rel_l2={r_t:.3e}")
+    if k_ramp == 0.0:
+        assert_close(got[rows], ref, "bf16", "fast launch with a short last tile")
+        max_abs, rel = errors(got, got_safe)
+        log(f"    fast vs running-max: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+        assert rel <= 1e-3 and max_abs <= 2e-3
+    else:
+        # bounds as in test_fast_launch_redoes_blocks_whose_weights_grow
+        max_abs, rel = errors(got[rows], ref)
+        assert rel <= 5e-3 and max_abs <= 5e-2
+        assert r_t <= 5e-3 and m_t <= 5e-2
+
+
 def test_stage_attend_matches_fwd_bitwise():
     grid, heads = (5, 9, 11), 2
     x = make_qkv(495, heads, 128, 400, "bf16")
