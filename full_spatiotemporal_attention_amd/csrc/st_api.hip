@@ -172,6 +172,12 @@ size_t cross_table_bytes(int d) {
     return table_bytes_for(1, 1, 1, t_only);
 }
 
+// bf16 cross-attention workspace after the table: the fp16 key tiles, then the fast launch's
+// flags (8 bytes per 256-row query block and head).
+size_t cross_tiles_bytes(int n_kv, int heads) {
+    return align_up(st::attn_stage_elems(heads, n_kv, 1) * 2, kWsAlign);
+}
+
 st_status hip_fail(hipError_t e) {
     g_last_hip_error = (int)e;
     return ST_ERR_HIP;
@@ -579,7 +585,7 @@ size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dty
     const size_t table = cross_table_bytes(d);
     if (dtype == ST_F32) return (d >= 2 && !(d & 1) && d <= 128) ? table : 0;
     if (dtype != ST_BF16 || d != 128) return 0;
-    return table + align_up(st::attn_stage_elems(heads, n_kv, 1) * 2, kWsAlign);
+    return table + cross_tiles_bytes(n_kv, heads) + align_up(st::attn_flag_bytes(heads, n_q, 1), kWsAlign);
 }
 
 st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,
@@ -627,8 +633,9 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
         uint16_t* kt = (uint16_t*)(ws + cross_table_bytes(d));
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
         if (e != hipSuccess) return hip_fail(e);
+        uint8_t* flags = (uint8_t*)(ws + cross_table_bytes(d) + cross_tiles_bytes(n_kv, heads));
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out,
-                                        nullptr, table, g, heads, L, nullptr, stream);
+                                        nullptr, table, g, heads, L, flags, stream);
     } else {
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
                                 table, g, heads, d, f32_layout(1, n_q, 0, 1, n_kv, 0, 1), stream);

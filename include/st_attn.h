@@ -230,7 +230,8 @@ st_status st_rope3d_apply(const void* x, void* y, int T, int H, int W, int n_tex
  *   q, out  [n_q][heads][d];  k, v  [n_kv][heads][d];  out must not overlap q, k or v.
  *   ST_BF16: d == 128, numerics as st_attn3d_fwd.  ST_F32: even d <= 128.
  *   Workspace (caller-owned, 256-byte aligned): st_attn_cross_workspace_bytes bytes, holding a
- *   table of zero angles (d/2 + 1 entries) and, for bf16, the fp16 key tiles.
+ *   table of zero angles (d/2 + 1 entries) and, for bf16, the fp16 key tiles and 8 bytes of flags
+ *   per 256-row query block and head (scratch of the attention launches, rewritten every call).
  * ------------------------------------------------------------------------------------------- */
 size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dtype dtype);
 st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,
