@@ -103,6 +103,16 @@ struct AttnParams {
     float scale_log2;      // log2(e) / sqrt(D)
     WinMap win;            // window mode only: segment s is window s, rows via win_origin/offset
     uint8_t* item_flags;   // 8 bytes per item: written by the fast launch, read by the guard launch
+    // Key split (fast launch of staged self-attention only): with k_split = 2 every query tile
+    // is two items, keys [0, split_tiles) and [split_tiles, k_tiles) of its sequence; the first
+    // writes part_a and lse, the second part_b and lse_b (fp32, so that the result is rounded to
+    // bf16 once, in the merge launch that combines them).  The guard launch (which never splits)
+    // reads both items' flags.
+    int k_split;
+    int split_tiles;
+    float* part_a;         // key split: each half's normalised output in fp32, [q rows][heads][D]
+    float* part_b;
+    float* lse_b;
 };
 
 struct PrepParams {
@@ -195,10 +205,20 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
     // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
     for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
-        // Guard launch: only the items the fast launch flagged.
-        if (p.item_flags && *reinterpret_cast<const unsigned long long*>(p.item_flags + 8ll * item) == 0)
-            continue;
         const int logical = xcd_remap(item, p.total_wg);
+        // Guard launch: only the items the fast launch flagged.  Its flags are by item number, or,
+        // after a key split (two items per query tile), by logical item: both halves are checked.
+        if (p.item_flags) {
+            const unsigned long long* fl = reinterpret_cast<const unsigned long long*>(p.item_flags);
+            bool redo;
+            if (p.k_split > 1) {
+                const int l0 = 2 * (logical - logical % p.q_tiles) + logical % p.q_tiles;
+                redo = (fl[l0] | fl[l0 + p.q_tiles]) != 0;
+            } else {
+                redo = fl[item] != 0;
+            }
+            if (!redo) continue;
+        }
         const int qt = logical % p.q_tiles;
         const int rest = logical / p.q_tiles;
         const int seg = rest % p.n_segs;
@@ -657,7 +677,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
 // for about 13 % less energy per product on random operands, and the kernel runs power-limited.
 // Its read addresses take more registers (8 V and 4 K bases), which the running-max kernel's
 // rescaling code has no room for.
-template <bool WIN>
+template <bool WIN, bool SPLIT>
 __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[LDS_BYTES];
     // 32 KB beside the tiles: in window mode the byte offset of each V row of the window; otherwise
@@ -682,15 +702,22 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
     for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
         const int logical = xcd_remap(item, p.total_wg);
         const int qt = logical % p.q_tiles;
-        const int rest = logical / p.q_tiles;
+        int rest = logical / p.q_tiles;
+        int half = 0;   // key split: which run of the sequence's key tiles this item takes
+        if constexpr (SPLIT) {
+            half = rest & 1;
+            rest >>= 1;
+        }
         const int seg = rest % p.n_segs;
         const int head = rest / p.n_segs;
-        const int seg_base = seg * p.seg_len;   // first key buffer row of the sequence
+        const int t0 = half * p.split_tiles;   // first key tile of the item
+        // From here on "the sequence" is the item's run of keys: from key row t0 * BN to the end.
+        const int seg_base = seg * p.seg_len + t0 * BN;   // first key buffer row of the run
         const int win0 = WIN ? win_origin(seg, p.win) : 0;   // window mode: grid row of local row 0
-        const int seg_len = p.seg_len;
+        const int seg_len = p.seg_len - t0 * BN;
         const int q_len = p.q_len;
         const long long row_stride = (long long)p.heads * D;
-        const int ntiles = p.k_tiles;
+        const int ntiles = SPLIT ? (half ? p.k_tiles - p.split_tiles : p.split_tiles) : p.k_tiles;
 
         const int tid = threadIdx.x;
         const int lane = tid & 63;
@@ -704,7 +731,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
         const int dr0 = 8 * wave + (lane >> 4);
         const int pc = lane & 15;
         const uint16_t* vhead = p.v + (long long)head * D;
-        const long long ktile0 = ((long long)head * p.n_segs + seg) * ntiles;
+        const long long ktile0 = ((long long)head * p.n_segs + seg) * p.k_tiles + t0;
         uint32_t k_src_off[2];   // staged: byte offset of the lane's chunk inside a K~ tile
         int v_chunk[2];          // element offset of the lane's logical chunk inside a V row
         uint32_t vch2[2];        // the same in bytes
@@ -1089,6 +1116,38 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fast_kernel(AttnParams p) {
         // workgroup's LDS is released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+        if constexpr (SPLIT) {
+            // A half of a key split.  Its coordinates again, from an opaque copy of the item number
+            // (kept from before the loop they would hold registers through it): flags are indexed
+            // by logical item (the guard reads both halves of a query tile), and the output is the
+            // half's normalised rows in fp32, 16 bytes per lane and block, with its log-sum-exp.
+            int item_e = item;
+            asm volatile("" : "+s"(item_e));
+            const int logical_e = xcd_remap(item_e, p.total_wg);
+            const bool second = ((logical_e / p.q_tiles) & 1) != 0;
+            float* const lsep = second ? p.lse_b : p.lse;
+            float* const part = second ? p.part_b : p.part_a;
+            {
+                const bool flagged = __any(!(l_run[0] < OVF_SUM) || !(l_run[1] < OVF_SUM));
+                if (lane == 0) p.item_flags[8ll * logical_e + wave] = flagged ? 1 : 0;
+            }
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                const float l_tot = xquad_sum(l_run[qb]);
+                const float inv = 1.0f / l_tot;
+                if (q_valid[qb] && lg == 0)
+                    lsep[(long long)q_row[qb] * p.heads + head] = m_run[qb] * 0.6931471805599453f + __logf(l_tot);
+                if (q_valid[qb]) {
+                    float* const op = part + q_row[qb] * row_stride + (long long)head * D + 4 * lg;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db)
+                        *reinterpret_cast<float4*>(op + 16 * db) =
+                            make_float4(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv, oacc[db][qb][2] * inv,
+                                        oacc[db][qb][3] * inv);
+                }
+            }
+            continue;
+        }
         {
             // Never rescaled, a lane's partial row sums bound every weight it has used.
             const bool flagged = __any(!(l_run[0] < OVF_SUM) || !(l_run[1] < OVF_SUM));
@@ -1243,6 +1302,11 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     p.scale_log2 = 1.4426950408889634f / sqrtf((float)D);
     p.win = WinMap{};
     p.item_flags = nullptr;
+    p.k_split = 1;
+    p.split_tiles = p.k_tiles;
+    p.part_a = nullptr;
+    p.part_b = nullptr;
+    p.lse_b = nullptr;
     return p;
 }
 
@@ -1250,14 +1314,19 @@ AttnParams make_params(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
 // cover all D/2 pairs (text rows read the position-0 entries).
 bool geom_covers_head(const RopeGeom& g) { return g.pairs[0] + g.pairs[1] + g.pairs[2] == D / 2; }
 
-// Workgroups of a persistent launch: one per CU (each holds 128 KB of LDS), rounded down to a
-// multiple of the 8 XCDs, and no more than there are items.
-int persistent_grid(int total) {
+// Compute units of the current device, rounded down to a multiple of the 8 XCDs.
+int cu_count() {
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
         ncu = 256;
-    ncu -= ncu % 8;
+    return ncu - ncu % 8;
+}
+
+// Workgroups of a persistent launch: one per CU (each holds 128 KB of LDS), no more than there are
+// items.
+int persistent_grid(int total) {
+    const int ncu = cu_count();
     return total < ncu ? total : ncu;
 }
 
@@ -1267,7 +1336,22 @@ int persistent_grid(int total) {
 // 512 text keys (12,288 pairs) 130 -> 126 us, in A/Bs on one box.
 constexpr long long kFastMinTiles = 4096;
 
-// Staged (FUSED = false) launches: with `flags` (8 bytes per item, attn_flag_bytes), the fast
+// Key split of the fast launch: two items per query tile, each over one half of the key tiles,
+// when the last round of the persistent grid would leave most CUs idle.  At 5x30x52 x 12 heads
+// the 372 items fill 1.45 rounds of 256 CUs; 744 half-items fill 2.9.  The halves are merged by
+// their log-sum-exp (one HBM pass over the output).  Self-attention over staged keys only.
+int key_split(long long items, int k_tiles) {
+    if (items * k_tiles < kFastMinTiles || k_tiles < 32) return 1;
+    const long long ncu = cu_count();
+    const double eff1 = (double)items / (double)(ncu * ((items + ncu - 1) / ncu));
+    const double eff2 = (double)(2 * items) / (double)(ncu * ((2 * items + ncu - 1) / ncu));
+    return eff2 >= eff1 + 0.15 ? 2 : 1;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Staged (FUSED = false) launches: with `flags` (attn_flag_bytes: 8 bytes per item, and the buffers
+// of a key split), the fast
 // kernel followed by the guard launch of the safe kernel; otherwise the safe kernel alone.
 template <bool FUSED, bool WIN>
 hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
@@ -1276,10 +1360,41 @@ hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
     if constexpr (!FUSED) {
         if (flags && (long long)p.total_wg * p.k_tiles >= kFastMinTiles) {
             p.item_flags = flags;
-            hipLaunchKernelGGL((attn_fast_kernel<WIN>), grid, dim3(NTHREADS), 0, stream, p);
+            const int ks = WIN ? 1 : key_split(p.total_wg, p.k_tiles);
+            AttnParams pf = p;
+            const long long rows_heads = (long long)p.n_segs * p.q_len * p.heads;
+            if (ks > 1) {
+                // Scratch after the flags (attn_flag_bytes): the second half's output and the
+                // log-sum-exp of both halves.
+                uint8_t* cur = flags + align256((size_t)p.total_wg * 2 * 8);
+                pf.part_a = reinterpret_cast<float*>(cur);
+                cur += align256((size_t)rows_heads * D * 4);
+                pf.part_b = reinterpret_cast<float*>(cur);
+                cur += align256((size_t)rows_heads * D * 4);
+                pf.lse = reinterpret_cast<float*>(cur);
+                cur += align256((size_t)rows_heads * 4);
+                pf.lse_b = reinterpret_cast<float*>(cur);
+                pf.k_split = 2;
+                pf.split_tiles = (p.k_tiles + 1) / 2;
+                pf.total_wg = 2 * p.total_wg;
+            }
+            if (ks > 1)
+                hipLaunchKernelGGL((attn_fast_kernel<false, true>), dim3(persistent_grid(pf.total_wg)), dim3(NTHREADS), 0,
+                                   stream, pf);
+            else
+                hipLaunchKernelGGL((attn_fast_kernel<WIN, false>), grid, dim3(NTHREADS), 0, stream, pf);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN>), grid, dim3(NTHREADS), 0, stream, p);
+            if (ks > 1) {
+                e = launch_merge2_f32_bf16(pf.part_a, pf.part_b, pf.lse, pf.lse_b, rows_heads, D, p.out, p.lse,
+                                           stream);
+                if (e != hipSuccess) return e;
+            }
+            // The guard redoes, over all keys and into out (after the merge), every query tile
+            // that one of its items flagged.
+            AttnParams pg = p;
+            pg.k_split = ks;
+            hipLaunchKernelGGL((attn_fwd_kernel<false, WIN>), grid, dim3(NTHREADS), 0, stream, pg);
             return hipGetLastError();
         }
     }
@@ -1295,8 +1410,12 @@ size_t attn_stage_elems(int heads, int kv_len, int n_segs) {
     return (size_t)heads * n_segs * k_tiles * BN * D;
 }
 
-size_t attn_flag_bytes(int heads, int q_len, int n_segs) {
-    return (size_t)((q_len + BM - 1) / BM) * n_segs * heads * 8;
+size_t attn_flag_bytes(int heads, int q_len, int kv_len, int n_segs) {
+    const long long items = (long long)((q_len + BM - 1) / BM) * n_segs * heads;
+    const int ks = key_split(items, (kv_len + BN - 1) / BN);
+    if (ks == 1) return (size_t)items * 8;
+    const size_t rows_heads = (size_t)n_segs * q_len * heads;
+    return align256((size_t)items * 2 * 8) + 2 * align256(rows_heads * D * 4) + 2 * align256(rows_heads * 4);
 }
 
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,

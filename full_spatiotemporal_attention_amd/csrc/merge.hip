@@ -145,7 +145,44 @@ hipError_t launch_merge(int n_parts, const T* const* o, const float* const* lse,
     return hipGetLastError();
 }
 
+// Two fp32 parts into bf16 (the key split of the fast attention launch, d = 128): 16 threads per
+// (row, head), 8 channels each.
+__global__ void __launch_bounds__(256) merge2_f32_bf16_kernel(const float* o0, const float* o1,
+                                                              const float* lse0, const float* lse1,
+                                                              long long rows_heads, uint16_t* out,
+                                                              float* lse_out) {
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rh = tid >> 4;
+    if (rh >= rows_heads) return;
+    const long long off = rh * 128 + (tid & 15) * 8;
+    const float4 a0 = *reinterpret_cast<const float4*>(o0 + off);
+    const float4 a1 = *reinterpret_cast<const float4*>(o0 + off + 4);
+    const float4 b0 = *reinterpret_cast<const float4*>(o1 + off);
+    const float4 b1 = *reinterpret_cast<const float4*>(o1 + off + 4);
+    const float l0 = lse0[rh], l1 = lse1[rh];
+    const float m = fmaxf(l0, l1);
+    const float e0 = expf(l0 - m), e1 = expf(l1 - m);
+    const float tot = e0 + e1;
+    const float w0 = e0 / tot, w1 = e1 / tot;
+    *reinterpret_cast<uint4*>(out + off) =
+        make_uint4(pack_bf16x2(fmaf(w0, a0.x, w1 * b0.x), fmaf(w0, a0.y, w1 * b0.y)),
+                   pack_bf16x2(fmaf(w0, a0.z, w1 * b0.z), fmaf(w0, a0.w, w1 * b0.w)),
+                   pack_bf16x2(fmaf(w0, a1.x, w1 * b1.x), fmaf(w0, a1.y, w1 * b1.y)),
+                   pack_bf16x2(fmaf(w0, a1.z, w1 * b1.z), fmaf(w0, a1.w, w1 * b1.w)));
+    if ((tid & 15) == 0 && lse_out) lse_out[rh] = m + logf(tot);
+}
+
 }  // namespace
+
+hipError_t launch_merge2_f32_bf16(const float* o0, const float* o1, const float* lse0, const float* lse1,
+                                  long long rows_heads, int d, uint16_t* out, float* lse_out,
+                                  hipStream_t stream) {
+    if (d != 128) return hipErrorInvalidValue;
+    const long long threads = rows_heads * 16;
+    hipLaunchKernelGGL(merge2_f32_bf16_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       o0, o1, lse0, lse1, rows_heads, out, lse_out);
+    return hipGetLastError();
+}
 
 hipError_t launch_merge_bf16(int n_parts, const uint16_t* const* o, const float* const* lse,
                              long long rows_heads, int d, uint16_t* out, float* lse_out,

@@ -184,8 +184,9 @@ st_status hip_fail(hipError_t e) {
 }
 
 // Byte layout of the bf16 staged workspace: [table][K~ tiles][item flags], each 256-aligned.  The
-// flags (8 bytes per 256-row query block of each sequence and head) are scratch of the attention
-// launches; sequences are self-attention ones (query rows = key rows = seg_len).
+// flags (8 bytes per 256-row query block of each sequence and head, and the buffers of a key split
+// when the attention launch splits) are scratch of the attention launches; sequences are
+// self-attention ones (query rows = key rows = seg_len).
 struct StageLayout {
     size_t table_bytes;
     size_t tiles_bytes;
@@ -199,7 +200,7 @@ StageLayout stage_layout(int T, int H, int W, int heads, int seg_len, int n_segs
     StageLayout L;
     L.table_bytes = table_bytes_for(T, H, W, split);
     L.tiles_bytes = align_up(st::attn_stage_elems(heads, seg_len, n_segs) * 2, kWsAlign);
-    L.flags_bytes = with_flags ? align_up(st::attn_flag_bytes(heads, seg_len, n_segs), kWsAlign) : 0;
+    L.flags_bytes = with_flags ? align_up(st::attn_flag_bytes(heads, seg_len, seg_len, n_segs), kWsAlign) : 0;
     L.total = L.table_bytes + L.tiles_bytes + L.flags_bytes;
     return L;
 }
@@ -585,7 +586,7 @@ size_t st_attn_cross_workspace_bytes(int n_q, int n_kv, int heads, int d, st_dty
     const size_t table = cross_table_bytes(d);
     if (dtype == ST_F32) return (d >= 2 && !(d & 1) && d <= 128) ? table : 0;
     if (dtype != ST_BF16 || d != 128) return 0;
-    return table + cross_tiles_bytes(n_kv, heads) + align_up(st::attn_flag_bytes(heads, n_q, 1), kWsAlign);
+    return table + cross_tiles_bytes(n_kv, heads) + align_up(st::attn_flag_bytes(heads, n_q, n_kv, 1), kWsAlign);
 }
 
 st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q, int n_kv,

@@ -190,10 +190,11 @@ hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uin
 // elements), then launch_attn_bf16_staged reads them together with V.
 // Fused mode: launch_attn_bf16_fused reads K directly and rotates it on every tile load.
 // `lse`, when not null, receives [q rows][heads] log-sum-exp of the scaled scores.
-// `flags` (attn_flag_bytes(heads, q_len, n_segs) bytes of device memory, or null): scratch of the
-// fast launch and its guard launch; with null only the kernel that tracks the running max runs.
+// `flags` (attn_flag_bytes(heads, q_len, kv_len, n_segs) bytes of device memory, or null): scratch
+// of the fast launch and its guard launch (flags, and for a key split the second half's output and
+// both halves' log-sum-exp); with null only the kernel that tracks the running max runs.
 size_t attn_stage_elems(int heads, int kv_len, int n_segs);
-size_t attn_flag_bytes(int heads, int q_len, int n_segs);
+size_t attn_flag_bytes(int heads, int q_len, int kv_len, int n_segs);
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
                          int heads, const SeqLayout& L, hipStream_t stream);
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
@@ -243,6 +244,10 @@ constexpr int kMaxMergeParts = 16;
 hipError_t launch_merge_bf16(int n_parts, const uint16_t* const* o, const float* const* lse,
                              long long rows_heads, int d, uint16_t* out, float* lse_out,
                              hipStream_t stream);
+// Two fp32 parts into bf16 output, d = 128 (the key split of the fast attention launch).
+hipError_t launch_merge2_f32_bf16(const float* o0, const float* o1, const float* lse0, const float* lse1,
+                                  long long rows_heads, int d, uint16_t* out, float* lse_out,
+                                  hipStream_t stream);
 hipError_t launch_merge_f32(int n_parts, const float* const* o, const float* const* lse,
                             long long rows_heads, int d, float* out, float* lse_out,
                             hipStream_t stream);

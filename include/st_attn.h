@@ -96,7 +96,10 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  *           its first 64 keys only and flags in the workspace any block of 256 query rows whose
  *           softmax row sums (taken against that offset) reach 2^64, infinity included; the second
  *           redoes only flagged blocks with a running maximum over every 64 keys.  Attention over
- *           fewer than 32768 (block, 64-key tile) pairs runs the second kind alone.
+ *           fewer than 4096 (block, 64-key tile) pairs runs the second kind alone.  When the
+ *           blocks would fill the chip's CUs badly (e.g. 31 blocks x 12 heads on 256 CUs), the
+ *           first launch splits every block's keys in two halves, kept apart with their
+ *           log-sum-exp in the workspace, and a merge launch combines them before the second.
  * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
  * fp16 for the score product, so every rotated q/k entry must stay below 65504 in magnitude
  * (inputs with |x| < 2^15 are always safe); softmax weights multiply V in bf16.
@@ -105,7 +108,9 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
 
 /* Workspace bytes st_attn3d_fwd (and stage/attend) need; 0 if the arguments are invalid.
  * ST_BF16: table + heads x ceil(N/64) x 64 x d x 2 bytes (K tiles) + heads x ceil(N/256) x 8
- * bytes (block flags), each part 256-byte aligned; ST_F32: table. */
+ * bytes (block flags), each part 256-byte aligned; with a key split (above) the flags double and
+ * N x heads x (8 d + 8) bytes follow them (both halves' fp32 outputs and log-sum-exp).
+ * ST_F32: table. */
 size_t st_attn3d_workspace_bytes(int T, int H, int W, int n_text, int heads, int d,
                                  const int rope_split[3], st_dtype dtype);
 

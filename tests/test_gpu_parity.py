@@ -223,9 +223,11 @@ def test_fast_launch_agrees_with_running_max_kernel():
     kernels evaluate the same weights; they differ only in the order of their fp32 sums (and so
     in a few roundings of weights and outputs to bf16).  Each meets the parity bar against the
     oracle on sampled rows, and the two agree to a fifth of the relative-L2 bar everywhere."""
+    # 4 heads: 64 blocks x 4 heads = 256 items fill the chip's CUs once, so the fast launch does not
+    # split keys (with 2 heads it would; see test_fast_launch_key_split)
     n = 8 * 32 * 64
-    log(f"  fast launch vs running-max kernel grid={FAST_GRID} heads=2 dtype=bf16 seed=330")
-    x = make_qkv(n, 2, 128, 330, "bf16")
+    log(f"  fast launch vs running-max kernel grid={FAST_GRID} heads=4 dtype=bf16 seed=330")
+    x = make_qkv(n, 4, 128, 330, "bf16")
     q, k, v = to_device(x)
     fast = fa.attn3d(q, k, v, FAST_GRID)
     safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
@@ -236,9 +238,9 @@ def test_fast_launch_agrees_with_running_max_kernel():
     log(f"    fast vs running-max: max_abs={max_abs:.3e} rel_l2={rel:.3e} identical={same:.3f}")
     assert rel <= 1e-3 and max_abs <= 2e-3
     rows = sample_rows(n, n, 2048, 256, 330)
-    ref = oracle.full_attention_ref(x.q, x.k, x.v, FAST_GRID, 0, WAN, 10000.0, rows=rows, heads=[0, 1])
-    assert_close(got_fast[rows], ref, "bf16", "fast launch")
-    assert_close(got_safe[rows], ref, "bf16", "running-max kernel")
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, FAST_GRID, 0, WAN, 10000.0, rows=rows, heads=[0, 3])
+    assert_close(got_fast[rows][:, [0, 3]], ref, "bf16", "fast launch")
+    assert_close(got_safe[rows][:, [0, 3]], ref, "bf16", "running-max kernel")
 
 
 @pytest.mark.parametrize("q_mult,k_ramp", [(2.0, 1.5), (6.0, 3.0)])
@@ -300,6 +302,46 @@ def test_fast_launch_short_last_tile(q_mult, k_ramp):
         max_abs, rel = errors(got[rows], ref)
         assert rel <= 5e-3 and max_abs <= 5e-2
         assert r_t <= 5e-3 and m_t <= 5e-2
+
+
+# 5x30x52 = 7,800 tokens x 12 heads (the 17-frame clip): 31 query blocks x 12 heads = 372 items,
+# 1.45 rounds of 256 CUs, so the fast launch splits every block's 122 key tiles into two halves of
+# 61 (744 items) and merges the halves by their log-sum-exp before the guard launch.
+SPLIT_GRID = (5, 30, 52)
+
+
+@pytest.mark.parametrize("q_mult,k_ramp", [(1.0, 0.0), (6.0, 3.0)])
+def test_fast_launch_key_split(q_mult, k_ramp):
+    """Sampled rows of three heads against the oracle, all rows against the running-max kernel
+    alone (no split), and two runs with the same bits.  With growing key norms the second half's sums pass 2^64, the
+    guard redoes those blocks over all keys after the merge, and the result still meets the bar."""
+    n, heads = 5 * 30 * 52, 12
+    log(f"  key split of the fast launch grid={SPLIT_GRID} heads={heads} q_mult={q_mult} k_ramp={k_ramp}")
+    x = make_qkv(n, heads, 128, 334, "bf16", q_mult=q_mult, k_ramp=k_ramp)
+    q, k, v = to_device(x)
+    fast = fa.attn3d(q, k, v, SPLIT_GRID)
+    again = fa.attn3d(q, k, v, SPLIT_GRID)
+    safe, _ = fa.attn3d_partial(q, k, v, SPLIT_GRID, q_begin=0, kv_begin=0)
+    torch.cuda.synchronize()
+    assert torch.equal(fast.view(torch.int16), again.view(torch.int16))
+    got, got_safe = host_f64(fast), host_f64(safe)
+    assert np.isfinite(got).all()
+    max_abs, rel = errors(got, got_safe)
+    log(f"    split fast launch vs running-max kernel: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    rows = sample_rows(n, n, 1560, 192, 334)
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, SPLIT_GRID, 0, WAN, 10000.0, rows=rows, heads=[0, 5, 11])
+    if k_ramp == 0.0:
+        # Each half rounds its weights to bf16 against its own offset (its first tile's row max),
+        # the unsplit kernel against one offset for all keys: the two differ by that rounding
+        # noise, well inside the bar, and each meets the bar against the oracle.
+        assert rel <= 5e-3 and max_abs <= 5e-3
+        assert_close(got[rows][:, [0, 5, 11]], ref, "bf16", "fast launch with a key split")
+        assert_close(got_safe[rows][:, [0, 5, 11]], ref, "bf16", "running-max kernel")
+    else:
+        assert rel <= 5e-3 and max_abs <= 5e-2
+        m2, r2 = errors(got[rows][:, [0, 5, 11]], ref)
+        log(f"    vs oracle: max_abs={m2:.3e} rel_l2={r2:.3e}")
+        assert r2 <= 5e-3 and m2 <= 5e-2
 
 
 def test_stage_attend_matches_fwd_bitwise():

@@ -303,11 +303,12 @@ def test_window_fast_launch_ragged_sampled():
 
 
 def test_window_over_whole_grid_fast_launch_bitwise():
-    """One window over a 16,384-token grid, 2 heads (64 blocks x 2 heads x 256 key tiles = 32768):
-    both calls take the fast launch, and with the identity row map they agree bit for bit."""
+    """One window over a 16,384-token grid, 4 heads (64 blocks x 4 heads x 256 key tiles): both
+    calls take the fast launch (256 items, one per CU, so full attention does not split its keys),
+    and with the identity row map they agree bit for bit."""
     grid = (8, 32, 64)
     log(f"  window grid={grid} window=grid vs attn3d (fast launch) dtype=bf16 seed=7650")
-    _, (q, k, v) = grid_inputs(grid, 0, 2, "bf16", 7650, WAN)
+    _, (q, k, v) = grid_inputs(grid, 0, 4, "bf16", 7650, WAN)
     a = fa.attn_window(q, k, v, grid, grid)
     b = fa.attn3d(q, k, v, grid)
     torch.cuda.synchronize()
