@@ -1,11 +1,13 @@
 """ctypes loader for libstattn.so (the in-tree HIP library) and its C signatures."""
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libstattn.so")
+POISON_LIB_PATH = os.path.join(PKG_DIR, "libstattn_ldspoison.so")   # LDS-poison debug build
 
 ST_OK = 0
 ST_BF16 = 0
@@ -88,6 +90,19 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.argtypes = args
     _LIB = lib
     return lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Route every call of the binding to another build of the library inside the block (e.g.
+    the LDS-poison debug build, POISON_LIB_PATH); the previous library is restored on exit."""
+    global _LIB
+    saved = _LIB
+    _LIB = None
+    try:
+        yield load(path)
+    finally:
+        _LIB = saved
 
 
 def split_arg(split) -> ctypes.Array:

@@ -3,6 +3,12 @@
 Usage: ``python -m full_spatiotemporal_attention_amd.build`` (or ``build()`` from Python).  Each
 HIP source is compiled to an object under ``_build/`` next to this file, then linked into
 ``libstattn.so`` in the package directory, which the ctypes binding loads.
+
+``build_lds_poison()`` makes a debug build of the same sources, ``libstattn_ldspoison.so``, with
+``ST_LDS_POISON`` defined: before every HBM -> LDS tile copy the destination bytes are first set to
+all-ones (NaN in fp16, bf16 and fp32), so that a read of a tile not ordered after its copy (a
+missing wait or barrier) yields NaN in the output instead of the previous tile's values.  Its
+outputs must equal the normal build's bit for bit.
 """
 from __future__ import annotations
 
@@ -18,6 +24,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libstattn.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+POISON_LIB_PATH = os.path.join(PKG_DIR, "libstattn_ldspoison.so")
 ARCH = "gfx950"
 
 SOURCES = ["st_api.hip", "rope.hip", "attn_bf16.hip", "attn_temporal.hip", "attn_f32.hip", "merge.hip",
@@ -47,17 +54,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (expected /opt/rocm/bin/hipcc)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libstattn.so; return the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _build_lib(lib_path: str, obj_dir: str, extra: list, verbose: bool) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     cc = hipcc()
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
-               os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC,
+               "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -72,16 +78,30 @@ def build(verbose: bool = False) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source and link libstattn.so; return the library path."""
+    return _build_lib(LIB_PATH, BUILD_DIR, [], verbose)
+
+
+def build_lds_poison(verbose: bool = False) -> str:
+    """Compile the LDS-poison debug build, libstattn_ldspoison.so; return its path."""
+    return _build_lib(POISON_LIB_PATH, os.path.join(BUILD_DIR, "lds_poison"), ["-DST_LDS_POISON=1"],
+                      verbose)
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--lds-poison" in sys.argv:
+        print(build_lds_poison(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -141,7 +141,23 @@ __device__ __forceinline__ int xcd_remap(int b, int total) {
 // lds + 16 L (global_load_lds_dwordx4, M0 = lds).  Written as inline asm so that the compiler does
 // not treat later LDS reads as waiting on it; callers wait for these copies explicitly with
 // s_waitcnt vmcnt before reading the data.
+//
+// LDS-poison debug build (ST_LDS_POISON defined): each lane first stores all-ones bits (NaN as
+// fp16, bf16 and fp32) to the 16 bytes its copy will write and waits for that store, so the copy
+// lands on poison.  A read of the tile that is not ordered after the copy (a missing vmcnt wait or
+// barrier) then returns NaN, which reaches the output, rather than the plausible values of the
+// tile the buffer held before.  Only the lanes that issue the copy store, exactly where it writes.
 __device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+#ifdef ST_LDS_POISON
+    {
+        const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        typedef uint32_t ones_t __attribute__((ext_vector_type(4)));
+        __attribute__((address_space(3))) ones_t* dst =
+            (__attribute__((address_space(3))) ones_t*)(uintptr_t)(lds + 16u * lane);
+        *dst = ones_t{~0u, ~0u, ~0u, ~0u};
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+#endif
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(base), "s"(lds)

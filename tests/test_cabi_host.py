@@ -55,6 +55,16 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_lds_poison_build_exports_every_declared_symbol():
+    """The LDS-poison debug build (same sources, ST_LDS_POISON) serves the same C ABI."""
+    import ctypes
+    if not os.path.exists(_lib.POISON_LIB_PATH):
+        pytest.skip(f"{_lib.POISON_LIB_PATH} not built")
+    dbg = ctypes.CDLL(_lib.POISON_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
+
+
 def test_status_strings_and_version(lib):
     for code in range(9):
         assert lib.st_status_str(code)
