@@ -202,23 +202,41 @@ __global__ void __launch_bounds__(NTHREADS, 1) attn_fwd_kernel(AttnParams p) {
     __shared__ uint32_t win_vrow[WIN ? WIN_TABLE : 1];   // window mode: byte offset of each V row
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
 
+    // Guard launch: only the items the fast launch flagged.  Its flags are by item number, or,
+    // after a key split (two items per query tile), by logical item: both halves are checked.
+    auto flagged = [&](int item) {
+        const unsigned long long* fl = reinterpret_cast<const unsigned long long*>(p.item_flags);
+        if (p.k_split > 1) {
+            const int logical = xcd_remap(item, p.total_wg);
+            const int l0 = 2 * (logical - logical % p.q_tiles) + logical % p.q_tiles;
+            return (fl[l0] | fl[l0 + p.q_tiles]) != 0;
+        }
+        return fl[item] != 0;
+    };
+    if (p.item_flags) {
+        // The threads read the flags of all of the workgroup's items at once (one load latency
+        // instead of one per item); a workgroup with nothing to redo ends here.
+        int any = 0;
+        for (int item = blockIdx.x + (int)threadIdx.x * (int)gridDim.x; item < p.total_wg;
+             item += NTHREADS * (int)gridDim.x)
+            any |= flagged(item) ? 1 : 0;
+        // One vote per wave in the tile buffer (not yet in use; the LDS is otherwise full).
+        uint32_t* const votes = reinterpret_cast<uint32_t*>(lds_raw);
+        const bool wave_any = __ballot(any) != 0;
+        if ((threadIdx.x & 63) == 0) votes[threadIdx.x >> 6] = wave_any ? 1u : 0u;
+        __syncthreads();
+        uint32_t all = 0;
+#pragma unroll
+        for (int w = 0; w < NTHREADS / 64; ++w) all |= votes[w];
+        __syncthreads();   // every wave has read the votes before tile copies overwrite them
+        if (!all) return;
+    }
+
     // Persistent: workgroup b takes items b, b + G, b + 2G, ... (G = gridDim.x, a multiple of 8),
     // each through the XCD remap, so the items an XCD runs at one time are neighbouring tiles.
     for (int item = blockIdx.x; item < p.total_wg; item += gridDim.x) {
         const int logical = xcd_remap(item, p.total_wg);
-        // Guard launch: only the items the fast launch flagged.  Its flags are by item number, or,
-        // after a key split (two items per query tile), by logical item: both halves are checked.
-        if (p.item_flags) {
-            const unsigned long long* fl = reinterpret_cast<const unsigned long long*>(p.item_flags);
-            bool redo;
-            if (p.k_split > 1) {
-                const int l0 = 2 * (logical - logical % p.q_tiles) + logical % p.q_tiles;
-                redo = (fl[l0] | fl[l0 + p.q_tiles]) != 0;
-            } else {
-                redo = fl[item] != 0;
-            }
-            if (!redo) continue;
-        }
+        if (p.item_flags && !flagged(item)) continue;
         const int qt = logical % p.q_tiles;
         const int rest = logical / p.q_tiles;
         const int seg = rest % p.n_segs;
