@@ -180,9 +180,11 @@ def run_legs(legs, q, k, v, out, full_ms, stream, dev):
                         stream, reps)
             fflop = (4.0 * GRID[0] * (GRID[1] * GRID[2]) ** 2 * HEADS * D
                      + 4.0 * GRID[1] * GRID[2] * GRID[0] ** 2 * HEADS * D)
-            extras[leg] = {"ms": round(ms, 4), "flop": fflop,
-                           "full_over_factorized_time": round(full_ms / ms, 3),
-                           "full_over_factorized_flop": round(flop / fflop, 3)}
+            # Whole path (staging, spatial stage, temporal stage) against the bf16 peak; the
+            # temporal stage is HBM-bound, so this fraction is a blend of two rooflines.
+            extras[leg] = dict(_mfma_rate(fflop, ms), flop=fflop,
+                               full_over_factorized_time=round(full_ms / ms, 3),
+                               full_over_factorized_flop=round(flop / fflop, 3))
         elif leg == "rope_apply":
             rws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
             rout = torch.empty_like(q)
