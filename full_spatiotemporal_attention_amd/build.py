@@ -4,7 +4,8 @@ Usage: ``python -m full_spatiotemporal_attention_amd.build`` (or ``build()`` fro
 HIP source is compiled to an object under ``_build/`` next to this file, then linked into
 ``libstattn.so`` in the package directory, which the ctypes binding loads.
 
-``build_lds_poison()`` makes a debug build of the same sources, ``libstattn_ldspoison.so``, with
+``build()`` also makes (and ``build_lds_poison()`` makes alone) a debug build of the same sources,
+``libstattn_ldspoison.so``, with
 ``ST_LDS_POISON`` defined: before every HBM -> LDS tile copy the destination bytes are first set to
 all-ones (NaN in fp16, bf16 and fp32), so that a read of a tile not ordered after its copy (a
 missing wait or barrier) yields NaN in the output instead of the previous tile's values.  Its
@@ -12,6 +13,7 @@ outputs must equal the normal build's bit for bit.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -47,6 +49,16 @@ HIPCC_FLAGS = [
 ]
 
 
+def source_hash() -> str:
+    """Hash of every source and header the library is built from (12 hex digits)."""
+    h = hashlib.sha256()
+    for path in ([os.path.join(CSRC, f) for f in SOURCES] + [os.path.join(CSRC, "st_internal.h"),
+                                                            os.path.join(INCLUDE, "st_attn.h")]):
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:12]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -62,8 +74,8 @@ def _build_lib(lib_path: str, obj_dir: str, extra: list, verbose: bool) -> str:
     for src in SOURCES:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC,
-               "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, f'-DST_SOURCE_HASH="{source_hash()}"',
+               "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
@@ -89,9 +101,13 @@ def _build_lib(lib_path: str, obj_dir: str, extra: list, verbose: bool) -> str:
     return lib_path
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libstattn.so; return the library path."""
-    return _build_lib(LIB_PATH, BUILD_DIR, [], verbose)
+def build(verbose: bool = False, lds_poison: bool = True) -> str:
+    """Compile every HIP source and link libstattn.so, and (by default) the LDS-poison debug build
+    beside it from the same sources; return the library path."""
+    path = _build_lib(LIB_PATH, BUILD_DIR, [], verbose)
+    if lds_poison:
+        build_lds_poison(verbose)
+    return path
 
 
 def build_lds_poison(verbose: bool = False) -> str:
@@ -105,3 +121,4 @@ if __name__ == "__main__":
         print(build_lds_poison(verbose="-v" in sys.argv))
     else:
         print(build(verbose="-v" in sys.argv))
+        print(POISON_LIB_PATH)

@@ -49,7 +49,8 @@ def build(verbose: bool = False) -> str:
     for src in _b.SOURCES:
         obj = os.path.join(OUT_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [cc, *_b.HIPCC_FLAGS, *_b.SOURCE_FLAGS.get(src, []), *HOST_SAN, "-I", _b.INCLUDE,
+        cmd = [cc, *_b.HIPCC_FLAGS, *_b.SOURCE_FLAGS.get(src, []), *HOST_SAN,
+               f'-DST_SOURCE_HASH="{_b.source_hash()}"', "-I", _b.INCLUDE,
                "-I", _b.CSRC, "-c", os.path.join(_b.CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)

@@ -846,6 +846,16 @@ const char* st_status_str(st_status s) {
 
 int st_last_hip_error(void) { return g_last_hip_error; }
 
-const char* st_version(void) { return "0.1.0"; }
+// The version names the sources the library was built from (a hash the build passes in) and
+// whether it is the LDS-poison debug build, so that two builds can be matched.
+#ifndef ST_SOURCE_HASH
+#define ST_SOURCE_HASH "unknown"
+#endif
+#ifdef ST_LDS_POISON
+#define ST_BUILD_TAG "+ldspoison"
+#else
+#define ST_BUILD_TAG ""
+#endif
+const char* st_version(void) { return "0.1.0+" ST_SOURCE_HASH ST_BUILD_TAG; }
 
 }  // extern "C"

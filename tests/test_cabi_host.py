@@ -63,13 +63,20 @@ def test_lds_poison_build_exports_every_declared_symbol():
     dbg = ctypes.CDLL(_lib.POISON_LIB_PATH)
     for name in declared_functions():
         assert hasattr(dbg, name), name
+    dbg.st_version.restype = ctypes.c_char_p
+    assert dbg.st_version().decode().endswith("+ldspoison")
 
 
 def test_status_strings_and_version(lib):
     for code in range(9):
         assert lib.st_status_str(code)
     assert lib.st_status_str(99) == b"unknown status"
-    assert lib.st_version() == b"0.1.0"
+    from full_spatiotemporal_attention_amd import build as _build
+    version = lib.st_version().decode()
+    assert version.startswith("0.1.0+")
+    if not os.environ.get("STATTN_LIB"):
+        # The in-tree library names the sources it was built from: these.
+        assert version == "0.1.0+" + _build.source_hash(), (version, "rebuild the library")
     assert lib.st_last_hip_error() == 0
 
 

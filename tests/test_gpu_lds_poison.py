@@ -37,8 +37,14 @@ def gpu_available():
     fa.library_path()
     if not os.path.exists(_lib.POISON_LIB_PATH):
         raise ImportError(f"{_lib.POISON_LIB_PATH} is missing: build it with "
-                          "`python -m full_spatiotemporal_attention_amd.build --lds-poison`")
-    log(f"  normal build {_lib.LIB_PATH}; poison build {_lib.POISON_LIB_PATH}")
+                          "`python -m full_spatiotemporal_attention_amd.build`")
+    normal = _lib.load().st_version().decode()
+    with _lib.use_library(_lib.POISON_LIB_PATH) as dbg:
+        poison = dbg.st_version().decode()
+    log(f"  normal build {_lib.LIB_PATH} ({normal}); poison build {_lib.POISON_LIB_PATH} ({poison})")
+    if poison != normal + "+ldspoison":
+        raise RuntimeError(f"the two builds come from different sources ({normal} vs {poison}): "
+                           "rebuild both with `python -m full_spatiotemporal_attention_amd.build`")
 
 
 def both_builds(fn):
