@@ -344,6 +344,31 @@ def test_fast_launch_key_split(q_mult, k_ramp):
         assert r2 <= 5e-3 and m2 <= 5e-2
 
 
+def test_fast_launch_key_split_odd_tile_count():
+    """The 17-frame grid with 40 text rows: 7,840 keys are 123 tiles, so the halves are 62 and 61
+    tiles and the second ends in a ragged tile.  Sampled rows of three heads (text rows included)
+    against the oracle, all rows against the running-max kernel alone."""
+    n_text, heads = 40, 12
+    n = 5 * 30 * 52 + n_text
+    log(f"  key split, odd tile count grid={SPLIT_GRID} n_text={n_text} heads={heads}")
+    # The workspace holds both halves' fp32 outputs and log-sum-exp only when the launch splits.
+    assert fa.attn3d_workspace_bytes(SPLIT_GRID, heads, n_text) >= n * heads * (8 * 128 + 8)
+    x = make_qkv(n, heads, 128, 335, "bf16")
+    q, k, v = to_device(x)
+    fast = fa.attn3d(q, k, v, SPLIT_GRID, n_text=n_text)
+    safe, _ = fa.attn3d_partial(q, k, v, SPLIT_GRID, q_begin=0, kv_begin=0, n_text=n_text)
+    torch.cuda.synchronize()
+    got, got_safe = host_f64(fast), host_f64(safe)
+    assert np.isfinite(got).all()
+    max_abs, rel = errors(got, got_safe)
+    log(f"    split fast launch vs running-max kernel: max_abs={max_abs:.3e} rel_l2={rel:.3e}")
+    assert rel <= 5e-3 and max_abs <= 5e-3
+    rows = np.union1d(sample_rows(n, n - n_text, 1560, 192, 335), np.arange(n - n_text, n))
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, SPLIT_GRID, n_text, WAN, 10000.0, rows=rows,
+                                    heads=[0, 6, 11])
+    assert_close(got[rows][:, [0, 6, 11]], ref, "bf16", "fast launch with an odd key split")
+
+
 def test_stage_attend_matches_fwd_bitwise():
     grid, heads = (5, 9, 11), 2
     x = make_qkv(495, heads, 128, 400, "bf16")

@@ -63,6 +63,20 @@ def test_cross_attention_wan_text_sampled():
     assert_close(host_f64(out)[rows], ref, "bf16", "cross 32760x512 sampled")
 
 
+def test_cross_attention_fast_launch_ragged():
+    """20,000 queries (the last query tile holds 32 rows) against 300 text keys (the last key tile
+    holds 44), 12 heads: 79 x 12 items of 5 key tiles take the fast launch.  Sampled rows plus the
+    whole short tile against the oracle."""
+    n_q, n_kv, heads = 20000, 300, 12
+    log(f"  cross n_q={n_q} n_kv={n_kv} heads={heads} dtype=bf16 seed=7250 (fast launch, ragged)")
+    qh, kh, vh, q, k, v = qkv_pair(n_q, n_kv, heads, "bf16", 7250)
+    out = fa.attn_cross(q, k, v)
+    torch.cuda.synchronize()
+    rows = np.union1d(sample_rows(n_q, n_q, 1560, 512, 7253), np.arange(19968, n_q))
+    ref = oracle.cross_attention_ref(qh, kh, vh, rows=rows)
+    assert_close(host_f64(out)[rows], ref, "bf16", "cross 20000x300 fast launch")
+
+
 # ---- partial attention and merge ---------------------------------------------------------------
 
 def grid_inputs(grid, n_text, heads, dtype, seed, split):
