@@ -126,6 +126,7 @@ struct PrepParams {
     int kv_pos_base;
     int k_tiles;
     WinMap win;            // window mode only
+    float2* table_fill;    // no video rows (g.Nv == 0): the table is written here, not read
 };
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -1267,8 +1268,18 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
     int t = 0, h = 0, w = 0;
     if (n < g.Nv) decode_pos(n, g, t, h, w);   // text rows: position (0, 0, 0), angles 0
     float2 cs[4];
+    if (g.Nv == 0 && p.table_fill) {
+        // No video rows (cross-attention): every angle is 0, so every entry is (1, 0).  The
+        // table is written here for the attention launch that follows instead of being read,
+        // which spares a launch of the table kernel.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cs[i] = p.table[pair_entry(4 * c + i, t, h, w, g)];
+        for (int i = 0; i < 4; ++i) cs[i] = make_float2(1.0f, 0.0f);
+        if (blockIdx.x == 0)
+            for (int e = threadIdx.x; e <= g.identity; e += blockDim.x) p.table_fill[e] = make_float2(1.0f, 0.0f);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cs[i] = p.table[pair_entry(4 * c + i, t, h, w, g)];
+    }
     const uint16_t* src = p.k + nb * row_stride + 8 * c;
     // Output row r of tile (head, seg, kt): ((head * n_segs + seg) * k_tiles + kt) * BN + r.
     const long long head_stride = (long long)p.n_segs * p.k_tiles * BN * D;
@@ -1437,11 +1448,12 @@ size_t attn_flag_bytes(int heads, int q_len, int kv_len, int n_segs) {
 }
 
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
-                         int heads, const SeqLayout& L, hipStream_t stream) {
+                         int heads, const SeqLayout& L, hipStream_t stream, float2* table_fill) {
     PrepParams p;
     p.k = k;
     p.kt = kt;
     p.table = table;
+    p.table_fill = table_fill;
     p.g = g;
     p.heads = heads;
     p.seg_len = L.kv_len;
@@ -1460,6 +1472,7 @@ hipError_t launch_k_prep_win(const uint16_t* k, uint16_t* kt, const float2* tabl
     p.k = k;
     p.kt = kt;
     p.table = table;
+    p.table_fill = nullptr;
     p.g = g;
     p.heads = heads;
     p.seg_len = L;

@@ -622,8 +622,7 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
     g.Nv = 0;
     char* ws = (char*)workspace;
     float2* table = (float2*)ws;
-    hipError_t e = st::launch_rope_table(g, 10000.0, table, stream);
-    if (e != hipSuccess) return hip_fail(e);
+    hipError_t e;
     if (dtype == ST_BF16) {
         st::SeqLayout L;
         L.n_segs = 1;
@@ -632,12 +631,15 @@ st_status st_attn_cross_fwd(const void* q, const void* k, const void* v, int n_q
         L.q_pos_base = 0;
         L.kv_pos_base = 0;
         uint16_t* kt = (uint16_t*)(ws + cross_table_bytes(d));
-        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
+        // The key staging launch writes the table of zero angles itself (no table launch).
+        e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream, table);
         if (e != hipSuccess) return hip_fail(e);
         uint8_t* flags = (uint8_t*)(ws + cross_table_bytes(d) + cross_tiles_bytes(n_kv, heads));
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out,
                                         nullptr, table, g, heads, L, flags, stream);
     } else {
+        e = st::launch_rope_table(g, 10000.0, table, stream);
+        if (e != hipSuccess) return hip_fail(e);
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, nullptr,
                                 table, g, heads, d, f32_layout(1, n_q, 0, 1, n_kv, 0, 1), stream);
     }
