@@ -544,6 +544,26 @@ def test_config_wan13b_81f_factorized_sampled():
     assert_close(np.concatenate(gs), np.concatenate(rs), "bf16", "21x30x52 factorised sampled per head")
 
 
+def test_hunyuan_factorized_sampled():
+    """Factorised attention at HunyuanVideo's shape: 33 x 45 x 80 latent grid, 24 heads, split
+    16/56/56.  T' = 33 takes the long temporal kernel (above 32 frames), here over 3,600 x 24
+    sequences; spatial frames of 3,600 tokens.  64 sampled rows of four heads against the oracle."""
+    grid, heads = (33, 45, 80), 24
+    n = grid[0] * grid[1] * grid[2]
+    log(f"  factorised {grid} heads={heads} split={HUN} sampled rows of heads 0, 7, 15, 23")
+    x = make_qkv(n, heads, 128, 2100, "bf16")
+    q, k, v = to_device(x)
+    got = host_f64(fa.attn_factorized(q, k, v, grid, rope_split=HUN))
+    del q, k, v
+    gs, rs = [], []
+    for hd in (0, 7, 15, 23):
+        rows = sample_rows_per_head(n, n, 3600, 64, 2103, hd)
+        sl = slice(hd, hd + 1)
+        rs.append(oracle.factorized_ref(x.q[:, sl], x.k[:, sl], x.v[:, sl], grid, HUN, rows=rows).ravel())
+        gs.append(got[rows, hd].ravel())
+    assert_close(np.concatenate(gs), np.concatenate(rs), "bf16", "33x45x80 factorised sampled")
+
+
 def test_config_wan14b_720p_sampled():
     grid, heads = (21, 45, 80), 40
     got, ref = run_full_sampled(grid, heads, 3000, 3003, row_scale=(0.5, 2.0))
