@@ -476,10 +476,13 @@ def test_non_finite_inputs_give_non_finite_rows(grid, heads):
 # Factorised
 # ------------------------------------------------------------------------------------------
 
+# Temporal kernels by T': up to 32 one block, 33 to 64 two blocks (33, 40, 64), beyond that the
+# looping kernel (70).
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("grid,heads,split", [
     ((3, 4, 6), 2, WAN), ((5, 7, 9), 3, WAN), ((1, 5, 7), 2, WAN), ((9, 1, 1), 2, WAN),
-    ((33, 3, 4), 2, HUN), ((40, 2, 3), 1, WAN), ((2, 16, 20), 2, WAN),
+    ((33, 3, 4), 2, HUN), ((40, 2, 3), 1, WAN), ((2, 16, 20), 2, WAN), ((64, 2, 2), 3, WAN),
+    ((70, 2, 3), 2, HUN),
 ])
 def test_factorized_small(dtype, grid, heads, split):
     T, H, W = grid
