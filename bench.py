@@ -102,8 +102,8 @@ def cpu_baseline(rows_per_head: int):
     }
 
 
-ALL_LEGS = ["wan13b_17f", "wan14b_720p", "hunyuan_joint", "factorized", "rope_apply", "fused_rope",
-            "cross_512", "merge2", "qkv_rope", "window_7x10x13"]
+ALL_LEGS = ["wan13b_17f", "wan14b_720p", "hunyuan_joint", "factorized", "factorized_hunyuan",
+            "rope_apply", "fused_rope", "cross_512", "merge2", "qkv_rope", "window_7x10x13"]
 
 
 def _timed(fn, stream, reps, warm=2):
@@ -185,6 +185,24 @@ def run_legs(legs, q, k, v, out, full_ms, stream, dev):
             extras[leg] = dict(_mfma_rate(fflop, ms), flop=fflop,
                                full_over_factorized_time=round(full_ms / ms, 3),
                                full_over_factorized_flop=round(flop / fflop, 3))
+        elif leg == "factorized_hunyuan":
+            # The factorised path at HunyuanVideo's latent grid (33 x 45 x 80, 24 heads, 16/56/56):
+            # T' = 33 takes the two-block temporal kernel.
+            hgrid, hheads, hsplit = (33, 45, 80), 24, (16, 56, 56)
+            hn = hgrid[0] * hgrid[1] * hgrid[2]
+            gh = torch.Generator(device=dev).manual_seed(SEED + 40)
+            hq, hk, hv = (torch.randn(hn, hheads, D, device=dev, generator=gh).to(torch.bfloat16)
+                          for _ in range(3))
+            hws = torch.empty(fa.attn_factorized_workspace_bytes(hgrid, hheads, D, hsplit), dtype=torch.uint8,
+                              device=dev)
+            hout = torch.empty_like(hq)
+            ms = _timed(lambda: fa.attn_factorized(hq, hk, hv, hgrid, hsplit, THETA, out=hout, workspace=hws),
+                        stream, 5, warm=1)
+            s_ = hgrid[1] * hgrid[2]
+            hflop = 4.0 * hgrid[0] * s_ * s_ * hheads * D + 4.0 * s_ * hgrid[0] ** 2 * hheads * D
+            extras[leg] = dict(_mfma_rate(hflop, ms), flop=hflop, grid=list(hgrid), heads=hheads,
+                               rope_split=list(hsplit), inputs="N(0,1) bf16, torch generator on the GPU")
+            del hq, hk, hv, hws, hout
         elif leg == "rope_apply":
             rws = torch.empty(fa.rope3d_table_bytes(GRID, SPLIT), dtype=torch.uint8, device=dev)
             rout = torch.empty_like(q)
