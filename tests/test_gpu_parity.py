@@ -483,6 +483,9 @@ def test_non_finite_inputs_give_non_finite_rows(grid, heads):
     ((3, 4, 6), 2, WAN), ((5, 7, 9), 3, WAN), ((1, 5, 7), 2, WAN), ((9, 1, 1), 2, WAN),
     ((33, 3, 4), 2, HUN), ((40, 2, 3), 1, WAN), ((2, 16, 20), 2, WAN), ((64, 2, 2), 3, WAN),
     ((70, 2, 3), 2, HUN),
+    # odd sequence counts (the two-block kernel's last workgroup holds one sequence), frames of
+    # more than one 64-row K~ tile
+    ((35, 3, 3), 1, HUN), ((33, 9, 9), 3, WAN),
 ])
 def test_factorized_small(dtype, grid, heads, split):
     T, H, W = grid
