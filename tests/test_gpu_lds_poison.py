@@ -10,7 +10,8 @@ poison stores change no arithmetic, so both builds must give identical bits.
 Covered, each through the C ABI: the fast launch (unsplit, key split, windows, cross-attention),
 the running-max kernel (small grids, partial results, fused K rotation), the factorised path (its
 spatial launch and the short temporal kernel, whose V rows arrive by the same copies) and the QKV
-projection (tiles of x and w, and its table copy).  The fp32 kernel and the long temporal kernel
+projection (tiles of x and w, and its table copy).  The two-block temporal kernel (T' = 33) also
+depends on a barrier: each wave of a pair copies half of the value rows the other reads.  The fp32 kernel and the long temporal kernel
 stage through registers within one wave (no copy to wait for) and are not affected by the flag.
 """
 import os
@@ -95,7 +96,8 @@ def test_fused_rotation():
     assert_same(ref, got, "attn3d_fused")
 
 
-@pytest.mark.parametrize("grid,heads", [((21, 30, 52), 12), ((5, 9, 11), 2)])
+@pytest.mark.parametrize("grid,heads", [((21, 30, 52), 12), ((5, 9, 11), 2),
+                                        ((33, 9, 9), 3)])   # T' = 33: two waves share V in LDS
 def test_factorized(grid, heads):
     n = grid[0] * grid[1] * grid[2]
     log(f"  attn_factorized grid={grid} heads={heads} seed=9120")
