@@ -1383,13 +1383,13 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // of a key split), the fast
 // kernel followed by the guard launch of the safe kernel; otherwise the safe kernel alone.
 template <bool FUSED, bool WIN>
-hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
+hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream, bool allow_split = true) {
     if (!geom_covers_head(p.g)) return hipErrorInvalidValue;
     const dim3 grid(persistent_grid(p.total_wg));
     if constexpr (!FUSED) {
         if (flags && (long long)p.total_wg * p.k_tiles >= kFastMinTiles) {
             p.item_flags = flags;
-            const int ks = WIN ? 1 : key_split(p.total_wg, p.k_tiles);
+            const int ks = (WIN || !allow_split) ? 1 : key_split(p.total_wg, p.k_tiles);
             AttnParams pf = p;
             const long long rows_heads = (long long)p.n_segs * p.q_len * p.heads;
             if (ks > 1) {
@@ -1437,6 +1437,10 @@ hipError_t launch(AttnParams p, uint8_t* flags, hipStream_t stream) {
 size_t attn_stage_elems(int heads, int kv_len, int n_segs) {
     const size_t k_tiles = (size_t)(kv_len + BN - 1) / BN;
     return (size_t)heads * n_segs * k_tiles * BN * D;
+}
+
+size_t attn_flag_bytes_unsplit(int heads, int q_len, int n_segs) {
+    return (size_t)((q_len + BM - 1) / BM) * n_segs * heads * 8;
 }
 
 size_t attn_flag_bytes(int heads, int q_len, int kv_len, int n_segs) {
@@ -1503,8 +1507,9 @@ hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uin
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, float* lse, const float2* table,
                                    const RopeGeom& g, int heads, const SeqLayout& L, uint8_t* flags,
-                                   hipStream_t stream) {
-    return launch<false, false>(make_params(q, kt, v, out, lse, table, g, heads, L), flags, stream);
+                                   hipStream_t stream, bool allow_split) {
+    return launch<false, false>(make_params(q, kt, v, out, lse, table, g, heads, L), flags, stream,
+                                allow_split);
 }
 
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -719,8 +719,10 @@ size_t st_attn3d_partial_workspace_bytes(int T, int H, int W, int n_text, int he
     if (kv_count < 1 || kv_count > n) return 0;
     if (dtype == ST_F32) return d <= 128 ? table_bytes_for(T, H, W, rope_split) : 0;
     if (dtype != ST_BF16 || d != 128) return 0;
-    // Partial results run the running-max kernel alone: no block flags.
-    return stage_layout(T, H, W, heads, kv_count, 1, rope_split, false).total;
+    // Table and key tiles, then the block flags of the fast launch for any query run (at most all
+    // n rows; the launch never splits its keys, whose buffers would grow with the query run).
+    return stage_layout(T, H, W, heads, kv_count, 1, rope_split, false).total +
+           align_up(st::attn_flag_bytes_unsplit(heads, (int)n, 1), kWsAlign);
 }
 
 st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int T, int H, int W,
@@ -778,8 +780,9 @@ st_status st_attn3d_partial_fwd(const void* q, const void* k, const void* v, int
         uint16_t* kt = (uint16_t*)(ws + table_bytes_for(T, H, W, rope_split));
         e = st::launch_k_prep((const uint16_t*)k, kt, table, g, heads, L, stream);
         if (e != hipSuccess) return hip_fail(e);
+        uint8_t* flags = (uint8_t*)(ws + stage_layout(T, H, W, heads, kv_count, 1, rope_split, false).total);
         e = st::launch_attn_bf16_staged((const uint16_t*)q, kt, (const uint16_t*)v, (uint16_t*)out, lse,
-                                        table, g, heads, L, nullptr, stream);
+                                        table, g, heads, L, flags, stream, /*allow_split=*/false);
     } else {
         e = st::launch_attn_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, lse,
                                 table, g, heads, d,

@@ -211,6 +211,8 @@ hipError_t launch_attn_bf16_win(const uint16_t* q, const uint16_t* kt, const uin
 // both halves' log-sum-exp); with null only the kernel that tracks the running max runs.
 size_t attn_stage_elems(int heads, int kv_len, int n_segs);
 size_t attn_flag_bytes(int heads, int q_len, int kv_len, int n_segs);
+// The flags alone (8 bytes per 256-row query block and head), for a launch that never splits.
+size_t attn_flag_bytes_unsplit(int heads, int q_len, int n_segs);
 // With no video rows (g.Nv == 0) and `table_fill` set, launch_k_prep reads no table: it writes
 // the table (every entry (1, 0)) into table_fill for the launches after it.
 hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, const RopeGeom& g,
@@ -218,7 +220,8 @@ hipError_t launch_k_prep(const uint16_t* k, uint16_t* kt, const float2* table, c
 hipError_t launch_attn_bf16_staged(const uint16_t* q, const uint16_t* kt, const uint16_t* v,
                                    uint16_t* out, float* lse, const float2* table,
                                    const RopeGeom& g, int heads, const SeqLayout& L, uint8_t* flags,
-                                   hipStream_t stream);
+                                   hipStream_t stream,
+                                   bool allow_split = true);
 hipError_t launch_attn_bf16_fused(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                   uint16_t* out, float* lse, const float2* table,
                                   const RopeGeom& g, int heads, const SeqLayout& L,

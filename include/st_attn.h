@@ -275,8 +275,11 @@ st_status st_qkv_rope_fwd(const void* x, const void* w, const void* bias, int T,
  * every row is rotated by its own global position.  Writes
  *   out [q_count][heads][d]  softmax over this run of keys times v (normalised, dtype of q)
  *   lse [q_count][heads]     float32 log sum_j exp(q~ . k~_j / sqrt(d)) over the run (natural log)
- * Workspace: st_attn3d_partial_workspace_bytes (0 for invalid arguments).  out, lse and the
- * workspace must not overlap each other or any input.
+ * ST_BF16 runs as st_attn3d_attend does (the fast launch and its guard from 4096 (block, key
+ * tile) pairs up), except that the keys are never split into halves.  Workspace:
+ * st_attn3d_partial_workspace_bytes (0 for invalid arguments): the angle table, the fp16 key
+ * tiles of the run and 8 bytes of block flags per 256 query rows and head, sized for a query run
+ * of every row.  out, lse and the workspace must not overlap each other or any input.
  *
  * st_attn_merge: combines n_parts (1..16) partial results over disjoint runs of keys for the same
  * query rows into the result over their union: lse = log sum_i exp(lse_i), out = sum_i

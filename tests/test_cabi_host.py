@@ -327,7 +327,9 @@ def test_cross_rejects_invalid_arguments(lib):
 def test_partial_workspace_bytes(lib):
     table = lib.st_rope3d_table_bytes(3, 4, 6, sp(44, 42, 42))
     tiles = 2 * ((30 + 63) // 64) * 64 * 128 * 2
-    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 30) == table + tiles
+    # block flags for a query run of all 72 rows: one 256-row block x 2 heads x 8 bytes, 256-aligned
+    flags = 256
+    assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 30) == table + tiles + flags
     assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 1, 30) == table
     assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 0) == 0
     assert lib.st_attn3d_partial_workspace_bytes(3, 4, 6, 0, 2, 128, sp(44, 42, 42), 0, 73) == 0

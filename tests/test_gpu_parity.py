@@ -230,7 +230,7 @@ def test_fast_launch_agrees_with_running_max_kernel():
     x = make_qkv(n, 4, 128, 330, "bf16")
     q, k, v = to_device(x)
     fast = fa.attn3d(q, k, v, FAST_GRID)
-    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
+    safe = fa.attn3d_fused(q, k, v, FAST_GRID)   # the running-max kernel at every size
     torch.cuda.synchronize()
     got_fast, got_safe = host_f64(fast), host_f64(safe)
     max_abs, rel = errors(got_fast, got_safe)
@@ -258,7 +258,7 @@ def test_fast_launch_redoes_blocks_whose_weights_grow(q_mult, k_ramp):
     # and the same rows from the running-max kernel alone agree to the same bound
     x = make_qkv(n, 2, 128, 331, "bf16", q_mult=q_mult, k_ramp=k_ramp)
     q, k, v = to_device(x)
-    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0)
+    safe = fa.attn3d_fused(q, k, v, FAST_GRID)   # the running-max kernel at every size
     torch.cuda.synchronize()
     m2, r2 = errors(got, host_f64(safe)[rows])
     log(f"    fast launch vs running-max kernel: max_abs={m2:.3e} rel_l2={r2:.3e}")
@@ -280,7 +280,7 @@ def test_fast_launch_short_last_tile(q_mult, k_ramp):
     x = make_qkv(n, 2, 128, 333, "bf16", q_mult=q_mult, k_ramp=k_ramp)
     q, k, v = to_device(x)
     fast = fa.attn3d(q, k, v, FAST_GRID, n_text=TAIL_TEXT)
-    safe, _ = fa.attn3d_partial(q, k, v, FAST_GRID, q_begin=0, kv_begin=0, n_text=TAIL_TEXT)
+    safe = fa.attn3d_fused(q, k, v, FAST_GRID, n_text=TAIL_TEXT)   # the running-max kernel
     again = fa.attn3d(q, k, v, FAST_GRID, n_text=TAIL_TEXT)
     torch.cuda.synchronize()
     assert torch.equal(fast.view(torch.int16), again.view(torch.int16))
@@ -321,7 +321,7 @@ def test_fast_launch_key_split(q_mult, k_ramp):
     q, k, v = to_device(x)
     fast = fa.attn3d(q, k, v, SPLIT_GRID)
     again = fa.attn3d(q, k, v, SPLIT_GRID)
-    safe, _ = fa.attn3d_partial(q, k, v, SPLIT_GRID, q_begin=0, kv_begin=0)
+    safe = fa.attn3d_fused(q, k, v, SPLIT_GRID)   # the running-max kernel, keys never split
     torch.cuda.synchronize()
     assert torch.equal(fast.view(torch.int16), again.view(torch.int16))
     got, got_safe = host_f64(fast), host_f64(safe)
@@ -356,7 +356,7 @@ def test_fast_launch_key_split_odd_tile_count():
     x = make_qkv(n, heads, 128, 335, "bf16")
     q, k, v = to_device(x)
     fast = fa.attn3d(q, k, v, SPLIT_GRID, n_text=n_text)
-    safe, _ = fa.attn3d_partial(q, k, v, SPLIT_GRID, q_begin=0, kv_begin=0, n_text=n_text)
+    safe = fa.attn3d_fused(q, k, v, SPLIT_GRID, n_text=n_text)   # the running-max kernel
     torch.cuda.synchronize()
     got, got_safe = host_f64(fast), host_f64(safe)
     assert np.isfinite(got).all()

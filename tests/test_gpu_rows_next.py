@@ -106,6 +106,28 @@ def test_partial_matches_oracle(dtype, grid, n_text, split, qb, qc, kb, kc):
     assert err <= LSE_TOL[dtype]
 
 
+def test_partial_fast_launch_with_lse():
+    """1,000 query rows (the last 256-row block holds 232) against a run of 8,192 keys of the
+    21x30x52 grid, 8 heads: 4 blocks x 8 heads x 128 key tiles take the fast launch, which writes
+    the log-sum-exp itself.  Two stretches of rows (the first block's start, the short block)
+    against the oracle, output and log-sum-exp."""
+    grid, heads = (21, 30, 52), 8
+    qb, qc, kb, kc = 12000, 1000, 4000, 8192
+    log(f"  partial (fast launch) grid={grid} heads={heads} q=[{qb},+{qc}) kv=[{kb},+{kc}) seed=7350")
+    x, (q, k, v) = grid_inputs(grid, 0, heads, "bf16", 7350, WAN)
+    o, lse = fa.attn3d_partial(q[qb:qb + qc].contiguous(), k[kb:kb + kc].contiguous(),
+                               v[kb:kb + kc].contiguous(), grid, q_begin=qb, kv_begin=kb)
+    torch.cuda.synchronize()
+    got_o, got_l = host_f64(o), host_f64(lse)
+    for a, b in ((0, 128), (872, 1000)):
+        ro, rl = oracle.partial_attention_ref(x.q[qb + a:qb + b], x.k[kb:kb + kc], x.v[kb:kb + kc], grid,
+                                              0, WAN, 10000.0, q_begin=qb + a, kv_begin=kb)
+        assert_close(got_o[a:b], ro, "bf16", f"partial fast launch o rows [{a}, {b})")
+        err = float(np.abs(got_l[a:b] - rl).max())
+        log(f"    partial fast launch lse rows [{a}, {b}) max_abs={err:.3e}")
+        assert err <= LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_merge_of_key_runs_equals_full_attention(dtype):
     grid, n_text, split, heads = (4, 9, 10), 20, WAN, 2
