@@ -403,7 +403,10 @@ __global__ void __launch_bounds__(SHORT_WAVES * 64) attn_temporal_short_kernel(S
 constexpr int MID_T = 64;
 constexpr int MID_SEQS = 2;   // sequences per workgroup (two waves each)
 
-__global__ void __launch_bounds__(MID_SEQS * 2 * 64) attn_temporal_mid_kernel(ShortParams p) {
+// At most 128 VGPRs, so that four waves share a SIMD (118 without spills; left free the compiler
+// takes 204, two waves per SIMD).  The compiler then issues fewer of a wave's loads ahead of its
+// first products, but the extra waves keep more of them in flight.
+__global__ void __launch_bounds__(MID_SEQS * 2 * 64, 4) attn_temporal_mid_kernel(ShortParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[MID_SEQS * MID_T * 256];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
