@@ -1296,11 +1296,21 @@ __global__ void __launch_bounds__(256) k_prep_kernel(PrepParams p) {
             const int hd = hb + h0 + 4 * k;
             if (hd < p.heads) {
                 uint32_t wd[4] = {raw[k].x, raw[k].y, raw[k].z, raw[k].w};
+                bool ovf = false;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float x0 = bf16_lo(wd[i]), x1 = bf16_hi(wd[i]);
                     rotate_pair(x0, x1, cs[i]);
                     wd[i] = pack_f16x2(x0, x1);
+                    ovf |= (wd[i] & 0x7fffu) == 0x7c00u || (wd[i] & 0x7fff0000u) == 0x7c000000u;
+                }
+                // A rotated key past fp16's range (the callers' precondition) would give some of
+                // its scores infinite terms whose signs the true products need not share, and the
+                // key could drop out unseen.  The whole row is made NaN instead, so every output
+                // row of the head shows it.  A row is the 16 lanes of this lane's group.
+                if ((__ballot(ovf) >> (lane & 48)) & 0xffffull) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) wd[i] = 0x7e007e00u;
                 }
                 *reinterpret_cast<uint4*>(dst + hd * head_stride) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
             }

@@ -101,8 +101,13 @@ st_status st_rope3d_table_build(int T, int H, int W, const int rope_split[3], fl
  *           first launch splits every block's keys in two halves, kept apart with their
  *           log-sum-exp in the workspace, and a merge launch combines them before the second.
  * st_attn3d_fwd = st_attn3d_stage + st_attn3d_attend.  The bf16 path rounds rotated q and k to
- * fp16 for the score product, so every rotated q/k entry must stay below 65504 in magnitude
- * (inputs with |x| < 2^15 are always safe); softmax weights multiply V in bf16.
+ * fp16 for the score product (q after its multiplication by log2(e)/sqrt(d)), so every rotated
+ * k entry must stay below 65504 in magnitude and every rotated q entry below 65504 * sqrt(128) /
+ * log2(e), about 5.1e5 (inputs with |x| < 2^15 are always safe); softmax weights multiply V in
+ * bf16.  Past those limits the result is NaN, not a wrong number: the staging step turns a key
+ * row with an entry past its limit into NaN, so every output row of that head is NaN, and a
+ * query row past its limit gives a NaN output row (its scores are all infinite or NaN).
+ * (st_attn3d_fwd_fused, which rotates K in the tile loads, does not make the key check.)
  * ST_F32 runs one fp32 kernel; its workspace is the angle table only.
  * ------------------------------------------------------------------------------------------- */
 

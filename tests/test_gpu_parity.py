@@ -472,6 +472,40 @@ def test_non_finite_inputs_give_non_finite_rows(grid, heads):
             np.testing.assert_array_equal(got[:, 1, :3], clean[:, 1, :3])
 
 
+@pytest.mark.parametrize("grid,heads", [((5, 9, 11), 2), (FAST_GRID, 2)])
+def test_inputs_past_fp16_range_give_nan_rows(grid, heads):
+    """Rotated k, and rotated q times log2(e)/sqrt(128), are rounded to fp16 for the score
+    product; staying inside fp16's range is the callers' precondition.  Past it the output is
+    NaN, never a wrong number.  A key row scaled by 2^17 (entries near 1e5) makes every row of its
+    head NaN: the staging step turns the row into NaN.  A query row scaled by 2^21 (near 2e6, past
+    65504 / 0.1275) makes its own output row NaN.  Everything else is bit-identical to the clean
+    run."""
+    T, H, W = grid
+    n = T * H * W
+    x = make_qkv(n, heads, 128, 404, "bf16")
+    q, k, v = to_device(x)
+    clean = host_f64(fa.attn3d(q, k, v, grid))
+    r = n // 3
+    for which, scale in (("k", 2.0 ** 17), ("q", 2.0 ** 21)):
+        log(f"  past fp16 range grid={grid} {which}[{r}, 1, :] * {scale:g}")
+        t = (k if which == "k" else q).clone()
+        t[r, 1] = t[r, 1] * scale             # a power of two: exact in bf16
+        got = host_f64(fa.attn3d(q, t, v, grid) if which == "k" else fa.attn3d(t, k, v, grid))
+        torch.cuda.synchronize()
+        bad = ~np.isfinite(got)
+        if which == "k":
+            assert bad[:, 1].all()
+            bad[:, 1] = False
+        else:
+            assert bad[r, 1].all()
+            bad[r, 1] = False
+            keep = np.ones(n, bool)
+            keep[r] = False
+            np.testing.assert_array_equal(got[keep, 1], clean[keep, 1])
+        assert not bad.any()
+        np.testing.assert_array_equal(got[:, 0], clean[:, 0])
+
+
 # ------------------------------------------------------------------------------------------
 # Factorised
 # ------------------------------------------------------------------------------------------
