@@ -180,9 +180,10 @@ def attn3d_noalloc(q, k, v, grid, n_text=0, rope_split=WAN_SPLIT, theta=10000.0,
         out = torch.empty_like(q)
     else:
         _check_out(out, q)
-    st = lib.st_attn3d_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
-                                   heads, d, _lib.split_arg(rope_split), float(theta), _dtype_code(q),
-                                   out.data_ptr(), _stream(q.device))
+    with torch.cuda.device(q.device):   # the library's scratch is that of the tensors' device
+        st = lib.st_attn3d_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), T, H, W, int(n_text),
+                                       heads, d, _lib.split_arg(rope_split), float(theta), _dtype_code(q),
+                                       out.data_ptr(), _stream(q.device))
     _lib.check("st_attn3d_fwd_noalloc", st)
     return out
 

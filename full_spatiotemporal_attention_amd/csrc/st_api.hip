@@ -374,14 +374,28 @@ st_status st_attn3d_fwd_noalloc(const void* q, const void* k, const void* v, int
     const size_t need = st_attn3d_workspace_bytes(T, H, W, n_text, heads, d, rope_split, dtype);
     if (need == 0) return ST_ERR_SHAPE;
     if (need > ST_NOALLOC_SCRATCH_BYTES) return ST_ERR_WORKSPACE;
-    hipError_t e;
+    // The scratch is per device: the stream's device (the current one for the null stream) is
+    // made current for the address lookup and the launches, and the caller's device restored.
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    int dev = cur;
+    if (stream) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(stream, &sd);
+        if (e != hipSuccess) return hip_fail(e);
+        dev = (int)sd;
+    }
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e);
     void* ws = scratch_on_current_device(&e);
-    if (!ws) return hip_fail(e);
     // The same launches as st_attn3d_fwd with the scratch as its workspace (no byte of it needs to
     // start at zero: the table and the staged tiles are written whole, every block flag is
     // rewritten by the attention launch that reads it).
-    return st_attn3d_fwd(q, k, v, T, H, W, n_text, heads, d, rope_split, theta, dtype, ws, need, out,
-                         stream);
+    const st_status r = ws ? st_attn3d_fwd(q, k, v, T, H, W, n_text, heads, d, rope_split, theta, dtype,
+                                           ws, need, out, stream)
+                           : hip_fail(e);
+    if (dev != cur) hipSetDevice(cur);
+    return r;
 }
 
 st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v, int T, int H, int W,

@@ -157,8 +157,10 @@ st_status st_attn3d_fwd_fused(const void* q, const void* k, const void* v,
  * workspace: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * The result is st_attn3d_fwd's, bit for bit (same launches); its workspace is a static device
  * array of ST_NOALLOC_SCRATCH_BYTES inside the library, of which each GPU holds one copy from the
- * library's load until the process ends.  The first call on a device takes the array's device
- * address (hipGetSymbolAddress, with that device current); no call allocates or frees anything.
+ * library's load until the process ends.  The array used is that of the stream's device (the
+ * current device for the null stream), which the call makes current while it runs and then
+ * restores.  The first call on a device takes the array's device address (hipGetSymbolAddress,
+ * with that device current); no call allocates or frees anything.
  *   Limit   st_attn3d_workspace_bytes(...) for the request must not exceed
  *           ST_NOALLOC_SCRATCH_BYTES (128 MiB: e.g. 21x30x52 tokens x 12 heads needs 100.7 MB);
  *           larger requests return ST_ERR_WORKSPACE with nothing enqueued.
