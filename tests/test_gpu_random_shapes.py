@@ -1,12 +1,14 @@
 """Seeded random shapes through every attention entry point, against the float64 oracle.
 
 The other GPU tests pick their shapes by hand, one for each edge a kernel was written for.  These
-cases draw grids, head counts, text rows, RoPE splits, windows and key runs from fixed seeds, so
-that every launch choice also meets shapes nobody chose:
+cases draw grids, head counts, text rows, RoPE splits, windows, key runs and projection widths
+from fixed seeds, so that every entry point and launch choice also meets shapes nobody chose:
 - the running-max kernel alone;
 - the fast launch with its guard, with and without the key split and its merge;
 - the window row map;
-- the temporal kernels for T' up to 32, up to 64 and longer.
+- the temporal kernels for T' up to 32, up to 64 and longer;
+- the QKV projection, the merge of 1 to 16 key runs, the stand-alone rotation (other head sizes
+  too) and the allocation-free entry (bit-identical to attn3d).
 
 Each case's parameters follow from its seed alone (`case_*` below) and are printed before it runs.
 The bar is the same as everywhere else: bf16 must meet max-abs 2e-2 and relative L2 5e-3 over the
@@ -19,6 +21,7 @@ import torch
 
 import oracle
 import full_spatiotemporal_attention_amd as fa
+from full_spatiotemporal_attention_amd import _lib
 from st_inputs import make_qkv, sample_rows, sample_rows_per_head
 from parity_util import assert_close, host_f64, log, to_device
 
@@ -248,3 +251,133 @@ def test_partial_random(seed, c):
         err = float(np.abs(got_l[a:b] - rl).max())
         log(f"    lse rows [{a}, {b}) max_abs={err:.3e}")
         assert err <= LSE_TOL["bf16"]
+
+
+# ---- the entry points around the attention kernels ---------------------------------------------
+
+def case_qkv(seed):
+    g = _rng(seed)
+    grid = _grid(g, 20000)
+    n_text = _int(g, 1, 200) if _int(g, 0, 2) == 1 else 0
+    return dict(grid=grid, n_text=n_text, heads=_int(g, 1, 10), split=_split(g),
+                bias=bool(_int(g, 0, 3)))
+
+
+def case_merge(seed):
+    g = _rng(seed)
+    grid = _grid(g, 3000, (1, 6), 20, 30)
+    n_text = _int(g, 1, 60) if _int(g, 0, 2) == 1 else 0
+    n = grid[0] * grid[1] * grid[2] + n_text
+    n_runs = min(_int(g, 1, 16), n)
+    cuts = sorted(set(int(c) for c in g.choice(np.arange(1, n), size=n_runs - 1, replace=False))) if n_runs > 1 else []
+    return dict(grid=grid, n_text=n_text, heads=_int(g, 1, 3), split=_split(g), cuts=[0] + cuts + [n])
+
+
+def case_rope(seed):
+    g = _rng(seed)
+    grid = _grid(g, 40000)
+    n_text = _int(g, 1, 300) if _int(g, 0, 2) == 1 else 0
+    if seed % 2 == 0:                            # another head size (bf16 serves d % 8 == 0)
+        d = 8 * _int(g, 1, 32)
+        dt = 2 * _int(g, 0, d // 2)
+        dh = 2 * _int(g, 0, (d - dt) // 2)
+        split = (dt, dh, d - dt - dh)
+    else:
+        split = _split(g)
+    n = grid[0] * grid[1] * grid[2] + n_text
+    return dict(grid=grid, n_text=n_text, heads=_heads(g, n, 12, 200000), split=split)
+
+
+def case_noalloc(seed):
+    g = _rng(seed)
+    grid = _grid(g, 30000)
+    n_text = _int(g, 1, 300) if _int(g, 0, 2) == 1 else 0
+    n = grid[0] * grid[1] * grid[2] + n_text
+    return dict(grid=grid, n_text=n_text, heads=_heads(g, n, 6, 90000), split=_split(g))
+
+
+QKV = [(s, case_qkv(s)) for s in range(8600, 8606)]
+MERGE = [(s, case_merge(s)) for s in range(8700, 8706)]
+ROPE = [(s, case_rope(s)) for s in range(8800, 8806)]
+NOALLOC = [(s, case_noalloc(s)) for s in range(8900, 8904)]
+
+
+@pytest.mark.parametrize("seed,c", QKV, ids=_ids(QKV))
+def test_qkv_rope_random(seed, c):
+    grid, n_text, heads, split = c["grid"], c["n_text"], c["heads"], c["split"]
+    n = grid[0] * grid[1] * grid[2] + n_text
+    ch = heads * 128
+    log(f"  qkv_rope seed={seed} grid={grid} n_text={n_text} heads={heads} (C={ch}) split={split} "
+        f"bias={c['bias']}")
+    g = _rng(seed + 1)
+    host = [make_bf16(g.standard_normal((n, ch))),
+            make_bf16(g.standard_normal((3 * ch, ch)) / np.sqrt(ch)),
+            make_bf16(0.1 * g.standard_normal(3 * ch)) if c["bias"] else None]
+    x, w, b = (None if a is None else torch.from_numpy(a).to(torch.bfloat16).cuda() for a in host)
+    q, k, v = fa.qkv_rope(x, w, grid, bias=b, n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, n - n_text, grid[1] * grid[2], 8 * ROWS_PER_HEAD, seed + 17)
+    refs = oracle.qkv_rope_ref(host[0], host[1], host[2], grid, n_text, split, 10000.0, rows=rows)
+    for name, got, ref in zip("qkv", (q, k, v), refs):
+        assert_close(host_f64(got)[rows], ref, "bf16", f"qkv_rope seed {seed} {name}")
+
+
+def make_bf16(a):
+    """float64 values rounded once to bf16, returned as float32 (the exact bf16 values)."""
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("seed,c", MERGE, ids=_ids(MERGE))
+def test_merge_random(seed, c):
+    grid, n_text, heads, split, cuts = c["grid"], c["n_text"], c["heads"], c["split"], c["cuts"]
+    log(f"  merge seed={seed} grid={grid} n_text={n_text} heads={heads} split={split} runs={len(cuts) - 1}")
+    n = cuts[-1]
+    x = make_qkv(n, heads, 128, seed, "bf16")
+    q, k, v = to_device(x)
+    parts = [fa.attn3d_partial(q, k[a:b].contiguous(), v[a:b].contiguous(), grid, q_begin=0,
+                               kv_begin=a, n_text=n_text, rope_split=split)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = fa.attn_merge(parts)
+    torch.cuda.synchronize()
+    rows = sample_rows(n, n - n_text, grid[1] * grid[2], 4 * ROWS_PER_HEAD, seed + 17)
+    ref = oracle.full_attention_ref(x.q, x.k, x.v, grid, n_text, split, 10000.0, rows=rows)
+    assert_close(host_f64(o)[rows], ref, "bf16", f"merge of {len(cuts) - 1} runs, seed {seed}")
+    _, rl = oracle.partial_attention_ref(x.q[rows[0]:rows[0] + 1], x.k, x.v, grid, n_text, split,
+                                         10000.0, q_begin=int(rows[0]))
+    err = float(np.abs(host_f64(lse)[rows[0]] - rl[0]).max())
+    log(f"    merged lse (row {rows[0]}) max_abs={err:.3e}")
+    assert err <= LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("seed,c", ROPE, ids=_ids(ROPE))
+def test_rope_apply_random(seed, c):
+    grid, n_text, heads, split = c["grid"], c["n_text"], c["heads"], c["split"]
+    d = sum(split)
+    nv = grid[0] * grid[1] * grid[2]
+    log(f"  rope3d_apply seed={seed} grid={grid} n_text={n_text} heads={heads} d={d} split={split}")
+    x = make_qkv(nv + n_text, heads, d, seed, "bf16")
+    q = to_device(x)[0]
+    y = host_f64(fa.rope3d_apply(q, grid, n_text=n_text, rope_split=split))
+    ref = oracle.rope3d_ref(x.q, grid, n_text, split)
+    # one rounding of the rotated value to bf16: |err| <= 2^-8 |ref| (+ fp32 noise)
+    bad = int((np.abs(y - ref) > np.abs(ref) * 2.0 ** -8 + 1e-6).sum())
+    log(f"    elements past one bf16 rounding: {bad}")
+    assert bad == 0
+    np.testing.assert_array_equal(y[nv:], host_f64(q)[nv:])   # text rows pass through
+
+
+@pytest.mark.parametrize("seed,c", NOALLOC, ids=_ids(NOALLOC))
+def test_noalloc_random(seed, c):
+    """The allocation-free entry against attn3d on the same inputs: the same launches on another
+    workspace, so the outputs are identical bit for bit."""
+    grid, n_text, heads, split = c["grid"], c["n_text"], c["heads"], c["split"]
+    n = grid[0] * grid[1] * grid[2] + n_text
+    limit = int(_lib.load().st_attn3d_noalloc_scratch_bytes())
+    while heads > 1 and fa.attn3d_workspace_bytes(grid, heads, n_text, 128, split) > limit:
+        heads -= 1
+    log(f"  attn3d_noalloc seed={seed} grid={grid} n_text={n_text} heads={heads} split={split}")
+    q, k, v = to_device(make_qkv(n, heads, 128, seed, "bf16"))
+    a = fa.attn3d_noalloc(q, k, v, grid, n_text=n_text, rope_split=split)
+    b = fa.attn3d(q, k, v, grid, n_text=n_text, rope_split=split)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
