@@ -15,6 +15,8 @@ The bar is the same as everywhere else: bf16 must meet max-abs 2e-2 and relative
 compared elements, and the fp32 mode 1e-5.  Large cases compare a seeded sample of query rows per
 head, edge rows included.  The partial-attention log-sum-exp is held to 1e-2 (bf16) and 1e-5 (fp32).
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -135,13 +137,21 @@ def case_partial(seed, large):
                 q_run=(qb, qc), kv_run=(kb, kc))
 
 
-FULL = [(s, case_full(s)) for s in range(8100, 8116)]
-FULL_F32 = [(s, case_full_f32(s)) for s in range(8150, 8155)]
-FACT = [(s, case_factorized(s, t)) for s, t in
-        zip(range(8200, 8209), [(1, 32), (33, 64), (65, 90)] * 3)]
-WINDOW = [(s, case_window(s, s % 2 == 0)) for s in range(8300, 8308)]
-CROSS = [(s, case_cross(s)) for s in range(8400, 8408)]
-PARTIAL = [(s, case_partial(s, s % 2 == 0)) for s in range(8500, 8508)]
+# ST_RANDOM_SHAPES_SCALE=k (default 1) runs k times as many cases per family for a wider sweep:
+# the committed seeds, then seeds from base + 100000 on.
+SCALE = max(1, int(os.environ.get("ST_RANDOM_SHAPES_SCALE", "1")))
+
+
+def _seeds(base, count):
+    return list(range(base, base + count)) + list(range(base + 100000, base + 100000 + count * (SCALE - 1)))
+
+
+FULL = [(s, case_full(s)) for s in _seeds(8100, 16)]
+FULL_F32 = [(s, case_full_f32(s)) for s in _seeds(8150, 5)]
+FACT = [(s, case_factorized(s, [(1, 32), (33, 64), (65, 90)][i % 3])) for i, s in enumerate(_seeds(8200, 9))]
+WINDOW = [(s, case_window(s, s % 2 == 0)) for s in _seeds(8300, 8)]
+CROSS = [(s, case_cross(s)) for s in _seeds(8400, 8)]
+PARTIAL = [(s, case_partial(s, s % 2 == 0)) for s in _seeds(8500, 8)]
 
 
 def _ids(cases):
@@ -296,10 +306,10 @@ def case_noalloc(seed):
     return dict(grid=grid, n_text=n_text, heads=_heads(g, n, 6, 90000), split=_split(g))
 
 
-QKV = [(s, case_qkv(s)) for s in range(8600, 8606)]
-MERGE = [(s, case_merge(s)) for s in range(8700, 8706)]
-ROPE = [(s, case_rope(s)) for s in range(8800, 8806)]
-NOALLOC = [(s, case_noalloc(s)) for s in range(8900, 8904)]
+QKV = [(s, case_qkv(s)) for s in _seeds(8600, 6)]
+MERGE = [(s, case_merge(s)) for s in _seeds(8700, 6)]
+ROPE = [(s, case_rope(s)) for s in _seeds(8800, 6)]
+NOALLOC = [(s, case_noalloc(s)) for s in _seeds(8900, 4)]
 
 
 @pytest.mark.parametrize("seed,c", QKV, ids=_ids(QKV))
