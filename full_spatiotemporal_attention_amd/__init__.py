@@ -41,8 +41,8 @@ _DTYPES = {torch.bfloat16: _lib.ST_BF16, torch.float32: _lib.ST_F32}
 
 
 def library_path() -> str:
-    _lib.load()
-    return _lib.LIB_PATH
+    """Path of the loaded library: the in-tree libstattn.so, or the build STATTN_LIB names."""
+    return _lib.loaded_path()
 
 
 def version() -> str:

@@ -67,6 +67,7 @@ class StError(RuntimeError):
 
 
 _LIB = None
+_LIB_LOADED_PATH = None
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -74,7 +75,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
 
     ``STATTN_LIB`` in the environment names another build of the same library (the sanitized
     debug build of build_sanitized.py); by default the in-tree libstattn.so is loaded."""
-    global _LIB
+    global _LIB, _LIB_LOADED_PATH
     if _LIB is not None:
         return _LIB
     if path is None:
@@ -89,20 +90,27 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn.restype = res
         fn.argtypes = args
     _LIB = lib
+    _LIB_LOADED_PATH = os.path.abspath(path)
     return lib
+
+
+def loaded_path() -> str:
+    """Path of the library the binding calls (loading it first if needed)."""
+    load()
+    return _LIB_LOADED_PATH
 
 
 @contextlib.contextmanager
 def use_library(path: str):
     """Route every call of the binding to another build of the library inside the block (e.g.
     the LDS-poison debug build, POISON_LIB_PATH); the previous library is restored on exit."""
-    global _LIB
-    saved = _LIB
+    global _LIB, _LIB_LOADED_PATH
+    saved, saved_path = _LIB, _LIB_LOADED_PATH
     _LIB = None
     try:
         yield load(path)
     finally:
-        _LIB = saved
+        _LIB, _LIB_LOADED_PATH = saved, saved_path
 
 
 def split_arg(split) -> ctypes.Array:

@@ -67,6 +67,18 @@ def test_lds_poison_build_exports_every_declared_symbol():
     assert dbg.st_version().decode().endswith("+ldspoison")
 
 
+def test_library_path_names_the_loaded_build(lib):
+    """library_path() reports the build the binding calls, also inside use_library()."""
+    import full_spatiotemporal_attention_amd as fa
+    if not os.path.exists(_lib.POISON_LIB_PATH):
+        pytest.skip(f"{_lib.POISON_LIB_PATH} not built")
+    before = fa.library_path()
+    with _lib.use_library(_lib.POISON_LIB_PATH) as dbg:
+        assert fa.library_path() == os.path.abspath(_lib.POISON_LIB_PATH)
+        assert dbg.st_version().decode().endswith("+ldspoison")
+    assert fa.library_path() == before
+
+
 def test_status_strings_and_version(lib):
     for code in range(9):
         assert lib.st_status_str(code)
