@@ -137,9 +137,9 @@ def case_partial(seed, large):
                 q_run=(qb, qc), kv_run=(kb, kc))
 
 
-# ST_RANDOM_SHAPES_SCALE=k (default 1) runs k times as many cases per family for a wider sweep:
-# the committed seeds, then seeds from base + 100000 on.
-SCALE = max(1, int(os.environ.get("ST_RANDOM_SHAPES_SCALE", "1")))
+# ST_RANDOM_SHAPES_SCALE=k (default 2) runs k times the base count of cases per family: the base
+# seeds, then seeds from base + 100000 on.  Larger k is a wider sweep.
+SCALE = max(1, int(os.environ.get("ST_RANDOM_SHAPES_SCALE", "2")))
 
 
 def _seeds(base, count):
