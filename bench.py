@@ -106,12 +106,26 @@ ALL_LEGS = ["wan13b_17f", "wan14b_720p", "hunyuan_joint", "factorized", "factori
             "rope_apply", "fused_rope", "cross_512", "merge2", "qkv_rope", "window_7x10x13"]
 
 
-def _timed(fn, stream, reps, warm=2):
-    """Average ms per call of fn() over `reps` back-to-back calls bracketed by HIP events on the
-    launch stream (after `warm` untimed calls)."""
+def _timed(fn, stream, reps, warm=2, min_ms=30.0):
+    """Average ms per call of fn() over at least `reps` back-to-back calls, and at least `min_ms`
+    of work, bracketed by HIP events on the launch stream.  Untimed calls first: `warm` of them,
+    then more until about `min_ms` of work has run, so that the clock has settled after the
+    previous leg (the chip runs power-limited, and a few milliseconds after a heavy leg a short
+    one measured up to 17 % slow)."""
+    import math
     import torch
     for _ in range(warm):
         fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    one = max(e0.elapsed_time(e1), 1e-3)
+    extra = max(0, math.ceil(min_ms / one) - warm - 1)
+    for _ in range(extra):
+        fn()
+    reps = max(reps, math.ceil(min_ms / one))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
